@@ -1,0 +1,16 @@
+"""MI355X (gfx950) attention forward: HIP kernels behind a C ABI (include/attn.h).
+
+Python entry points (same names as the C calls, without the ``attn_`` prefix):
+prefill_gqa_rope, decode_gqa, decode_mla, combine_splits, and the workspace
+size queries.  libattn.so is loaded on first use; every call raises
+ImportError if it has not been built (there is no other code path).
+"""
+from ._lib import AttnError, lib  # noqa: F401
+from .ops import (  # noqa: F401
+    combine_splits,
+    decode_gqa,
+    decode_gqa_workspace_bytes,
+    decode_mla,
+    decode_mla_workspace_bytes,
+    prefill_gqa_rope,
+)

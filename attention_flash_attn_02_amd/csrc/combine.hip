@@ -1,0 +1,81 @@
+// Split-softmax combine: merge per-split partial attention results.
+//
+// Each split s of a row carries its output normalised within the split,
+// o_s, and the natural-log log-sum-exp of its scaled scores, lse_s.  The
+// merged row is sum_s w_s o_s / sum_s w_s with w_s = exp(lse_s - max lse).
+// Folding two parts at a time with alpha = sigmoid(lse_b - lse_a),
+// o = (1 - alpha) o_a + alpha o_b (the merge rule of the fixed-budget
+// decode audit, section "A: group-entry queries and one joint history
+// scan") reaches the same result; the weighted sum does it in one pass.
+// Empty splits (lse = -inf) have weight 0; a row whose splits are all
+// empty is written as zeros.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o_part,
+                                                     const float* __restrict__ lse_part,
+                                                     void* __restrict__ o, int nsplit, int D,
+                                                     int out_dtype) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* lse = lse_part + (size_t)r * nsplit;
+  float mx = kNegInf;
+  for (int s = tid; s < nsplit; s += 64) mx = fmaxf(mx, lse[s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const size_t obase = (size_t)r * D;
+  if (mx == kNegInf) {
+    for (int d = tid; d < D; d += 64) store1(o, obase + d, out_dtype, 0.f);
+    return;
+  }
+  float wsum = 0.f;
+  for (int s = 0; s < nsplit; ++s) wsum += fast_exp2((lse[s] - mx) * kLog2e);
+  const float inv = 1.f / wsum;
+  const float* op = o_part + (size_t)r * nsplit * D;
+  for (int d = tid; d < D; d += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float w = fast_exp2((lse[s] - mx) * kLog2e);
+      acc = fmaf(w, op[(size_t)s * D + d], acc);
+    }
+    store1(o, obase + d, out_dtype, acc * inv);
+  }
+}
+
+void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
+                    int out_dtype, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3(R), dim3(64), 0, stream, o_part, lse_part, o, nsplit, D,
+                     out_dtype);
+}
+
+}  // namespace attn
+
+extern "C" attn_status attn_combine_splits(const float* o_part, const float* lse_part, void* o,
+                                           int R, int nsplit, int D, attn_dtype out_dtype,
+                                           hipStream_t stream) {
+  if (!o_part || !lse_part || !o) return ATTN_ERR_NULL;
+  if (R <= 0 || nsplit <= 0 || D <= 0 || D > 1024) return ATTN_ERR_SHAPE;
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_F16 && out_dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (!attn_host::aligned(o_part, 4) || !attn_host::aligned(lse_part, 4) ||
+      !attn_host::aligned(o, out_dtype == ATTN_F32 ? 4 : 2))
+    return ATTN_ERR_ALIGN;
+  attn::launch_combine(o_part, lse_part, o, R, nsplit, D, out_dtype, stream);
+  return attn_host::launch_status();
+}
+
+extern "C" const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer argument";
+    case ATTN_ERR_SHAPE: return "invalid or inconsistent shape";
+    case ATTN_ERR_DTYPE: return "unsupported dtype";
+    case ATTN_ERR_ALIGN: return "misaligned pointer";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}

@@ -1,0 +1,29 @@
+// Internal launchers shared between translation units of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+// Merge split partials o_part [R, nsplit, D] / lse_part [R, nsplit] into
+// o [R, D] (out_dtype) on `stream`.
+void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
+                    int out_dtype, hipStream_t stream);
+
+// Workspace layout of the decode calls: partial outputs first, then the
+// partial log-sum-exps, each 256-byte aligned.
+struct SplitWorkspace {
+  size_t o_bytes;
+  size_t lse_offset;
+  size_t total;
+};
+
+inline SplitWorkspace split_workspace(long long rows, long long nsplit, long long d) {
+  SplitWorkspace w;
+  w.o_bytes = (size_t)(rows * nsplit * d) * sizeof(float);
+  w.lse_offset = (w.o_bytes + 255) / 256 * 256;
+  w.total = w.lse_offset + ((size_t)(rows * nsplit) * sizeof(float) + 255) / 256 * 256;
+  return w;
+}
+
+}  // namespace attn

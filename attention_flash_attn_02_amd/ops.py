@@ -1,0 +1,120 @@
+"""Thin torch-facing wrappers over the C ABI (argument marshalling only).
+
+Every function takes device tensors, checks that they are contiguous CUDA
+(HIP) tensors of the expected dtype and shape, and passes raw pointers and
+torch's current stream to the library.  All arithmetic runs in the
+library's kernels.  Output tensors (and decode workspaces) may be passed in;
+otherwise they are allocated with torch.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.ATTN_F32, torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16,
+       torch.float8_e5m2: _lib.ATTN_FP8_E5M2}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
+def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_theta: float = 0.0,
+                     out_dtype=None, out=None, return_lse: bool = False, q_descale: float = 1.0,
+                     k_descale: float = 1.0, v_descale: float = 1.0, stream=None):
+    """attn_prefill_gqa_rope: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> o [B,Hq,S,D] (and lse [B,Hq,S])."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, S, D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if out_dtype is None:
+        out_dtype = torch.float16 if q.dtype == torch.float8_e5m2 else q.dtype
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if return_lse else None
+    code = _lib.lib().attn_prefill_gqa_rope(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
+        B, Hq, Hkv, S, D, _dtype_code(q), _dtype_code(out), float(softmax_scale), int(bool(causal)),
+        float(rope_theta), float(q_descale), float(k_descale), float(v_descale), _stream(stream))
+    _lib.check(code)
+    return (out, lse) if return_lse else out
+
+
+def decode_gqa_workspace_bytes(B, Hq, cap, D, split=0) -> int:
+    return int(_lib.lib().attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split))
+
+
+def decode_gqa(q, k_cache, v_cache, kv_len, softmax_scale: float, split: int = 0, out=None,
+               workspace=None, stream=None):
+    """attn_decode_gqa: q [B,Hq,D], caches [B,Hkv,cap,D], kv_len int32 [B] -> o [B,Hq,D]."""
+    B, Hq, D = q.shape
+    _, Hkv, cap, _ = k_cache.shape
+    if kv_len.dtype != torch.int32 or kv_len.shape != (B,):
+        raise ValueError("kv_len must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_gqa_workspace_bytes(B, Hq, cap, D, split)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    code = _lib.lib().attn_decode_gqa(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(kv_len, "kv_len"),
+        _dev(out, "out"), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        B, Hq, Hkv, D, cap, int(split), _dtype_code(q), float(softmax_scale), _stream(stream))
+    _lib.check(code)
+    return out
+
+
+def decode_mla_workspace_bytes(B, H, cap, d_latent, split=0) -> int:
+    return int(_lib.lib().attn_decode_mla_workspace_bytes(B, H, cap, d_latent, split))
+
+
+def decode_mla(q, kv_cache, kv_len, softmax_scale: float, d_latent: int = 448, split: int = 0,
+               out=None, workspace=None, stream=None):
+    """attn_decode_mla: q [B,H,dl+dr], cache [B,cap,dl+dr], kv_len int32 [B] -> o [B,H,dl]."""
+    B, H, dq = q.shape
+    cap = kv_cache.shape[1]
+    d_rope = dq - d_latent
+    if kv_len.dtype != torch.int32 or kv_len.shape != (B,):
+        raise ValueError("kv_len must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, H, d_latent), dtype=q.dtype, device=q.device)
+    need = decode_mla_workspace_bytes(B, H, cap, d_latent, split)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    code = _lib.lib().attn_decode_mla(
+        _dev(q, "q"), _dev(kv_cache, "kv_cache"), _dev(kv_len, "kv_len"), _dev(out, "out"),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), B, H, d_latent,
+        d_rope, cap, int(split), _dtype_code(q), float(softmax_scale), _stream(stream))
+    _lib.check(code)
+    return out
+
+
+def combine_splits(o_part, lse_part, out_dtype=torch.float32, out=None, stream=None):
+    """attn_combine_splits: o_part [R,nsplit,D] f32, lse_part [R,nsplit] f32 -> o [R,D]."""
+    R, ns, D = o_part.shape
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32 or lse_part.shape != (R, ns):
+        raise ValueError("o_part [R,nsplit,D] and lse_part [R,nsplit] must be float32")
+    if out is None:
+        out = torch.empty((R, D), dtype=out_dtype, device=o_part.device)
+    code = _lib.lib().attn_combine_splits(_dev(o_part, "o_part"), _dev(lse_part, "lse_part"),
+                                          _dev(out, "out"), R, ns, D, _dtype_code(out), _stream(stream))
+    _lib.check(code)
+    return out

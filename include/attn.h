@@ -1,0 +1,167 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) attention forward library.
+ *
+ * Scaled-dot-product attention forward with online softmax: causal GQA
+ * prefill with fused RoPE, split-context GQA decode against a static KV
+ * cache, absorbed-MLA decode over a 448-d latent plus 64-d RoPE cache, and
+ * the split-softmax combine step that both decode paths end with.
+ *
+ * Conventions shared by every call:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major arrays
+ *    with the head dimension innermost.  The caller owns every buffer,
+ *    including the workspace; the library allocates and frees nothing and
+ *    keeps no mutable global state, so calls are thread-safe.
+ *  - Calls only enqueue kernels on `stream` and return; nothing synchronises
+ *    with the host, so every call is legal inside hipGraph stream capture.
+ *  - Host-side argument checks run before anything is launched; on a
+ *    non-OK status nothing was enqueued.  A failed kernel launch returns
+ *    ATTN_ERR_LAUNCH.  Values that live in device memory (kv_len) cannot be
+ *    checked on the host: they are clamped to [0, cap] on the device, and a
+ *    sequence with kv_len == 0 gets an all-zero output row.
+ *  - Tensor pointers must be 16-byte aligned (lse pointers 4-byte aligned).
+ *  - softmax_scale multiplies q.k before the softmax (the caller passes
+ *    1/sqrt(head_dim) for the usual scaling).
+ *
+ * Sources (pages cited by title and section):
+ *  - "Lesson: shape adaptive attention negative 20260722", rows "What was
+ *    tried" and "Conditions": causal GQA prefill/decode with RoPE fused into
+ *    attention, one global tile configuration, eager vs graph replay.
+ *  - "Fixed-budget decode audit", sections "Which implementation was
+ *    tested" and "Setup and interpretation": split-context decode (split
+ *    128) against a static append cache (capacity 2056 for context 2048),
+ *    MLA with a 448-d latent + 64-d RoPE per token; section "A: group-entry
+ *    queries and one joint history scan": the softmax-part merge.
+ *  - Persistent-attention digest (hada.io), benchmark section: Z=4, H=32
+ *    forward in fp16 and fp8 e5m2 ("float8e5").
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    ATTN_ERR_SHAPE = 2,       /* a size is <= 0, inconsistent or too large     */
+    ATTN_ERR_DTYPE = 3,       /* unknown dtype or unsupported dtype combination */
+    ATTN_ERR_ALIGN = 4,       /* a pointer is not suitably aligned             */
+    ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required       */
+    ATTN_ERR_UNSUPPORTED = 6, /* valid request this build does not implement   */
+    ATTN_ERR_LAUNCH = 7       /* the HIP runtime rejected a kernel launch      */
+} attn_status;
+
+typedef enum attn_dtype {
+    ATTN_F32 = 0,
+    ATTN_F16 = 1,
+    ATTN_BF16 = 2,
+    ATTN_FP8_E5M2 = 3         /* OCP E5M2 bytes (1 sign, 5 exponent, 2 mantissa) */
+} attn_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_str(attn_status s);
+
+/* ------------------------------------------------------------------------ *
+ * Prefill: O = softmax(scale * rope(Q) rope(K)^T [+ causal mask]) V
+ *
+ * Operation: for query head h of sequence b, KV head g = h / (Hq/Hkv); with
+ * RoPE, rows of Q and K at position p are rotated in rotate-half pairs
+ * (i, i + D/2) by angle p * rope_theta^(-2i/D), positions 0..S-1; causal
+ * means key j is visible to query i iff j <= i.
+ *
+ *   q    [B, Hq,  S, D]  in_dtype
+ *   k, v [B, Hkv, S, D]  in_dtype
+ *   o    [B, Hq,  S, D]  out_dtype
+ *   lse  [B, Hq,  S]     float32, natural-log log-sum-exp of the scaled
+ *                        scores of each row; may be NULL (not written).
+ *
+ * in_dtype: ATTN_F32, ATTN_F16, ATTN_BF16 or ATTN_FP8_E5M2.
+ * out_dtype: ATTN_F32, ATTN_F16 or ATTN_BF16.  D: 64 or 128.
+ * rope_theta <= 0 disables RoPE (RoPE with fp8 input: ATTN_ERR_UNSUPPORTED).
+ * q_descale, k_descale multiply the scores and v_descale the output (per-
+ * tensor dequantisation factors; pass 1.0 for unscaled inputs).
+ * Math is fp32 with fp32 accumulation; 16-bit and fp8 inputs use MFMA.
+ * ------------------------------------------------------------------------ */
+attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, int B, int Hq, int Hkv, int S, int D,
+                                  attn_dtype in_dtype, attn_dtype out_dtype,
+                                  float softmax_scale, int causal, float rope_theta,
+                                  float q_descale, float k_descale, float v_descale,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Split-context GQA decode ("flash-decoding"): one new query token per
+ * sequence against a static KV cache.
+ *
+ *   q        [B, Hq, D]        dtype
+ *   k_cache  [B, Hkv, cap, D]  dtype (slot t holds the key of position t)
+ *   v_cache  [B, Hkv, cap, D]  dtype
+ *   kv_len   [B] int32, DEVICE memory: sequence b attends to slots
+ *            0..kv_len[b]-1 of its KV head (the new token's own key and
+ *            value are already in the cache); slots >= kv_len[b] are
+ *            never read, so they may hold anything, NaN included.
+ *   o        [B, Hq, D]        dtype
+ *   workspace: device scratch of at least attn_decode_gqa_workspace_bytes()
+ *            bytes, 256-byte aligned; contents on entry are ignored.
+ *
+ * The context is cut into splits of `split` slots aligned at slot 0
+ * (split <= 0 picks the library default, 128); each split's partial
+ * softmax is written to the workspace and merged by the combine step.
+ * dtype: ATTN_BF16 or ATTN_F16.  D: 128.  Hq/Hkv <= 16.  split: a multiple
+ * of 32 in [32, 1024].  Launches two kernels on `stream`.
+ * ------------------------------------------------------------------------ */
+size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int cap, int D, int split);
+attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* kv_len, void* o, void* workspace,
+                            size_t workspace_bytes, int B, int Hq, int Hkv, int D, int cap,
+                            int split, attn_dtype dtype, float softmax_scale,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Absorbed-MLA decode: H query heads share one latent cache row per token.
+ *
+ *   q        [B, H, d_latent + d_rope]    dtype, the absorbed query
+ *            [W_UK q_nope ; q_rope] (latent part first)
+ *   kv_cache [B, cap, d_latent + d_rope]  dtype, latent then RoPE part
+ *   kv_len   [B] int32, DEVICE memory (as for attn_decode_gqa)
+ *   o        [B, H, d_latent]             dtype: softmax(scale q c^T) c_lat
+ *   workspace: at least attn_decode_mla_workspace_bytes() bytes.
+ *
+ * Scores use all d_latent + d_rope dims; values are the latent part of the
+ * same rows.  dtype: ATTN_BF16 or ATTN_F16.  d_latent = 448, d_rope = 64,
+ * H <= 16.  split <= 0 picks the library default (256); otherwise a multiple
+ * of 32 in [32, 2048].  Launches two kernels on `stream`.
+ * ------------------------------------------------------------------------ */
+size_t attn_decode_mla_workspace_bytes(int B, int H, int cap, int d_latent, int split);
+attn_status attn_decode_mla(const void* q, const void* kv_cache, const int32_t* kv_len,
+                            void* o, void* workspace, size_t workspace_bytes, int B, int H,
+                            int d_latent, int d_rope, int cap, int split, attn_dtype dtype,
+                            float softmax_scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Split-softmax combine (the merge of softmax parts): for each of R rows,
+ *   o[r] = sum_s w_s o_part[r, s] / sum_s w_s,  w_s = exp(lse_part[r, s] - max_s lse_part[r, s]).
+ * This equals folding the pairwise merge alpha = sigmoid(lse_b - lse_a),
+ * o = (1 - alpha) o_a + alpha o_b over the parts.  A part with
+ * lse = -inf is empty and contributes nothing; a row whose parts are all
+ * empty gets zeros.
+ *
+ *   o_part   [R, nsplit, D] float32, each part normalised within itself
+ *   lse_part [R, nsplit]    float32, natural log
+ *   o        [R, D]         out_dtype (ATTN_F32, ATTN_F16 or ATTN_BF16)
+ * D: 1..1024.  The decode calls run this step themselves; it is exported so
+ * that it can be called and tested on its own.
+ * ------------------------------------------------------------------------ */
+attn_status attn_combine_splits(const float* o_part, const float* lse_part, void* o, int R,
+                                int nsplit, int D, attn_dtype out_dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,153 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/attn.h, and rejects bad arguments on the host before
+anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_flash_attn_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# Fake but 256-byte aligned device addresses: every call below must fail its
+# host-side checks before any use of them.
+P = 0x100000
+P2 = 0x200000
+ODD = 0x100002
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"attn_prefill_gqa_rope", "attn_decode_gqa", "attn_decode_mla", "attn_combine_splits",
+            "attn_status_str", "attn_decode_gqa_workspace_bytes",
+            "attn_decode_mla_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.attn_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.attn_status_str(99).decode() == "unknown status"
+
+
+def _prefill(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P2, lse=None, B=1, Hq=4, Hkv=2, S=16, D=64, in_dt=_lib.ATTN_BF16,
+             out_dt=_lib.ATTN_BF16, scale=0.125, causal=1, theta=0.0, qd=1.0, kd=1.0, vd=1.0)
+    a.update(kw)
+    return lib.attn_prefill_gqa_rope(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                     a["S"], a["D"], a["in_dt"], a["out_dt"], a["scale"], a["causal"],
+                                     a["theta"], a["qd"], a["kd"], a["vd"], None)
+
+
+def test_prefill_rejects(lib):
+    assert _prefill(lib, q=None) == 1
+    assert _prefill(lib, o=None) == 1
+    assert _prefill(lib, S=0) == 2
+    assert _prefill(lib, B=-1) == 2
+    assert _prefill(lib, Hq=6, Hkv=4) == 2
+    assert _prefill(lib, in_dt=7) == 3
+    assert _prefill(lib, out_dt=_lib.ATTN_FP8_E5M2) == 3
+    assert _prefill(lib, D=96) == 6
+    assert _prefill(lib, in_dt=_lib.ATTN_FP8_E5M2, out_dt=_lib.ATTN_F16, theta=10000.0) == 6
+    assert _prefill(lib, q=ODD) == 4
+    assert _prefill(lib, lse=P + 2) == 4
+    assert _prefill(lib, scale=float("nan")) == 2
+
+
+def _gqa(lib, ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, L=P, o=P2, ws=P, B=2, Hq=16, Hkv=4, D=128, cap=300, split=128,
+             dt=_lib.ATTN_BF16, scale=0.1)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_gqa_workspace_bytes(a["B"], a["Hq"], a["cap"], a["D"], a["split"])
+    return lib.attn_decode_gqa(a["q"], a["k"], a["v"], a["L"], a["o"], a["ws"], ws_bytes, a["B"], a["Hq"],
+                               a["Hkv"], a["D"], a["cap"], a["split"], a["dt"], a["scale"], None)
+
+
+def test_decode_gqa_rejects(lib):
+    assert _gqa(lib, L=None) == 1
+    assert _gqa(lib, cap=0) == 2
+    assert _gqa(lib, Hq=16, Hkv=3) == 2
+    assert _gqa(lib, D=64) == 6
+    assert _gqa(lib, Hq=64, Hkv=2) == 6            # 32 query heads per KV head
+    assert _gqa(lib, dt=_lib.ATTN_F32) == 6
+    assert _gqa(lib, dt=11) == 3
+    assert _gqa(lib, split=100) == 2
+    assert _gqa(lib, split=2048) == 2
+    assert _gqa(lib, ws=None) == 5
+    assert _gqa(lib, ws_bytes=1024) == 5
+    assert _gqa(lib, ws=P + 16) == 4
+    assert _gqa(lib, o=ODD) == 4
+
+
+def test_decode_gqa_workspace_size(lib):
+    # partial outputs [B*Hq, nsplit, D] f32 then lse [B*Hq, nsplit] f32, 256-byte aligned pieces
+    B, Hq, cap, D, split = 128, 16, 2056, 128, 128
+    ns = -(-cap // split)
+    o_bytes = B * Hq * ns * D * 4
+    lse_bytes = B * Hq * ns * 4
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split) == up(o_bytes) + up(lse_bytes)
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 0) == lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 128)
+    assert lib.attn_decode_gqa_workspace_bytes(0, Hq, cap, D, split) == 0
+
+
+def _mla(lib, ws_bytes=None, **kw):
+    a = dict(q=P, c=P, L=P, o=P2, ws=P, B=2, H=16, dl=448, dr=64, cap=300, split=128,
+             dt=_lib.ATTN_BF16, scale=0.07)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_mla_workspace_bytes(a["B"], a["H"], a["cap"], a["dl"], a["split"])
+    return lib.attn_decode_mla(a["q"], a["c"], a["L"], a["o"], a["ws"], ws_bytes, a["B"], a["H"], a["dl"],
+                               a["dr"], a["cap"], a["split"], a["dt"], a["scale"], None)
+
+
+def test_decode_mla_rejects(lib):
+    assert _mla(lib, q=None) == 1
+    assert _mla(lib, B=0) == 2
+    assert _mla(lib, dl=512, dr=0) == 6
+    assert _mla(lib, H=32) == 6
+    assert _mla(lib, dt=_lib.ATTN_FP8_E5M2) == 6
+    assert _mla(lib, split=48) == 2
+    assert _mla(lib, ws_bytes=16) == 5
+    assert _mla(lib, c=ODD) == 4
+
+
+def test_combine_rejects(lib):
+    f = lib.attn_combine_splits
+    assert f(None, P, P2, 4, 3, 128, _lib.ATTN_F32, None) == 1
+    assert f(P, P, P2, 0, 3, 128, _lib.ATTN_F32, None) == 2
+    assert f(P, P, P2, 4, 3, 2048, _lib.ATTN_F32, None) == 2
+    assert f(P, P, P2, 4, 3, 128, _lib.ATTN_FP8_E5M2, None) == 3
+    assert f(P + 1, P, P2, 4, 3, 128, _lib.ATTN_F32, None) == 4
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    import attention_flash_attn_02_amd as attn
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.prefill_gqa_rope(q, q, q, 0.125)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "libattn.so"))

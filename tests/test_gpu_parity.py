@@ -1,0 +1,262 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 CPU
+oracle on the same seeded inputs.
+
+Tolerances (max-abs over every output element, GPU output upcast to float64):
+fp32 1e-5, bf16 / fp16 2e-2, fp8 e5m2 inputs 8e-2.  Full-size workloads are
+checked on sampled rows that the oracle computes one by one, plus properties
+that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import (decode_gqa_inputs, decode_mla_inputs, prefill_inputs, split_partials,
+                       to_f64)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2, "fp8_e5m2": 8e-2}
+
+
+@pytest.fixture(scope="module")
+def attn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_flash_attn_02_amd as a
+    a.lib()
+    return a
+
+
+def _dev(*ts):
+    return [t.to("cuda") for t in ts]
+
+
+def _maxerr(gpu, want):
+    got = to_f64(gpu)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - want)))
+
+
+# ----------------------------------------------------------------------------
+# Prefill
+# ----------------------------------------------------------------------------
+def test_tiny_f32_full(attn):
+    """Tiny causal GQA prefill, fp32: B=1, Hq=4, Hkv=2, S=128, D=64, scale 1/8."""
+    q, k, v = prefill_inputs(1, 4, 2, 128, 64, "f32")
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / 8, causal=True, return_lse=True)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / 8, True, return_lse=True)
+    assert _maxerr(o, want) <= TOL["f32"]
+    assert _maxerr(lse, want_lse) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal,rope", [(True, True), (True, False), (False, True), (False, False)])
+@pytest.mark.parametrize("B,Hq,Hkv,S", [(2, 8, 2, 300), (1, 4, 4, 97), (1, 6, 3, 130)])
+def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S):
+    """Several tiles with a ragged tail, G = 4, 1 and 2; every output element checked."""
+    q, k, v = prefill_inputs(B, Hq, Hkv, S, D, dtype, seed=S + D)
+    theta = 10000.0 if rope else 0.0
+    scale = 1 / math.sqrt(D)
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=causal, rope_theta=theta, return_lse=True)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), scale, causal, theta, return_lse=True)
+    assert _maxerr(o, want) <= TOL[dtype]
+    assert _maxerr(lse, want_lse) <= 2e-2
+
+
+@pytest.mark.parametrize("S", [1, 2, 31, 32, 33, 64, 65])
+def test_prefill_short_sequences(attn, S):
+    q, k, v = prefill_inputs(1, 8, 2, S, 128, "bf16", seed=S)
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.088, causal=True, rope_theta=10000.0)
+    want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 0.088, True, 10000.0)
+    assert _maxerr(o, want) <= 2e-2
+    # row 0 sees only key 0: the output is exactly V[0] of its KV head (rounded to bf16 once)
+    assert torch.equal(o[0, :, 0].cpu(), v[0, :, 0].repeat_interleave(4, dim=0))
+
+
+def test_prefill_out_dtype_f32_and_G8(attn):
+    q, k, v = prefill_inputs(1, 16, 2, 150, 128, "bf16", seed=5)
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.09, causal=True, rope_theta=500.0, out_dtype=torch.float32)
+    want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 0.09, True, 500.0)
+    assert o.dtype == torch.float32
+    assert _maxerr(o, want) <= 2e-2
+
+
+def test_gqa_rope_full_size_sampled(attn):
+    """Causal GQA prefill with fused RoPE at full size: B=1, Hq=32, Hkv=8,
+    S=2048, D=128, bf16, theta 10000; sampled rows of every head."""
+    q, k, v = prefill_inputs(1, 32, 8, 2048, 128, "bf16")
+    scale = 1 / math.sqrt(128)
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=True, rope_theta=10000.0).cpu()
+    rows = [0, 1, 31, 32, 63, 64, 127, 128, 1000, 1023, 1024, 2046, 2047]
+    qn, kn, vn = to_f64(q), to_f64(k), to_f64(v)
+    worst = 0.0
+    for h in range(32):
+        want, _ = oracle.prefill_rows(qn, kn, vn, scale, True, 10000.0, 0, h, rows)
+        worst = max(worst, _maxerr(o[0, h, rows], want))
+    assert worst <= 2e-2
+    assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "fp8_e5m2"])
+@pytest.mark.parametrize("D,causal", [(64, False), (128, True)])
+@pytest.mark.parametrize("N", [1024, 4096, 16384])
+def test_mha_forward_sampled(attn, dtype, D, causal, N):
+    """MHA forward Z=4, H=32 (fp16 or fp8 e5m2 in, fp16 out): sampled rows of
+    sampled heads, including (0, 0) and (3, 31)."""
+    q, k, v = prefill_inputs(4, 32, 32, N, D, dtype, seed=N + D)
+    scale = 1 / math.sqrt(D)
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=causal, out_dtype=torch.float16).cpu()
+    rng = np.random.default_rng(N)
+    rows = sorted(set([0, 1, N // 2, N - 1] + list(rng.integers(0, N, 4))))
+    heads = [(0, 0), (3, 31), (1, 7), (2, 20)]
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    worst = 0.0
+    for z, h in heads:
+        want, _ = oracle.prefill_rows(qn, kn, vn, scale, causal, 0.0, z, h, rows)
+        worst = max(worst, _maxerr(o[z, h, rows], want))
+    assert worst <= TOL[dtype]
+
+
+def test_mha_forward_full_small(attn):
+    """fp8 e5m2 and fp16 at N=1024, D=64 non-causal: every element of two batches."""
+    for dtype in ("f16", "fp8_e5m2"):
+        q, k, v = prefill_inputs(1, 8, 8, 1024, 64, dtype, seed=3)
+        o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.125, causal=False, out_dtype=torch.float16)
+        want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 0.125, False)
+        assert _maxerr(o, want) <= TOL[dtype]
+
+
+def test_prefill_descales(attn):
+    q, k, v = prefill_inputs(1, 4, 4, 100, 64, "fp8_e5m2", seed=9)
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.125, causal=True, q_descale=0.5, k_descale=2.0,
+                              v_descale=0.25, out_dtype=torch.float32)
+    want = oracle.prefill(to_f64(q) * 0.5, to_f64(k) * 2.0, to_f64(v) * 0.25, 0.125, True)
+    assert _maxerr(o, want) <= 2e-2
+
+
+def test_prefill_deterministic(attn):
+    q, k, v = _dev(*prefill_inputs(1, 8, 2, 256, 128, "bf16", seed=1))
+    a = attn.prefill_gqa_rope(q, k, v, 0.09, causal=True, rope_theta=10000.0)
+    b = attn.prefill_gqa_rope(q, k, v, 0.09, causal=True, rope_theta=10000.0)
+    assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# GQA decode
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [1, 8, 128])
+def test_decode_gqa_config(attn, B):
+    """GQA decode: Hq=16, Hkv=4, D=128, context 2048 in capacity 2056, split
+    128, bf16; slots 2048..2055 hold NaN and must never be read."""
+    q, kc, vc, L = decode_gqa_inputs(B, 16, 4, 128, 2056, 2048, "bf16", nan_tail=True)
+    scale = 1 / math.sqrt(128)
+    o = attn.decode_gqa(*_dev(q, kc, vc, L), scale, split=128)
+    want = oracle.decode_gqa(to_f64(q), to_f64(kc), to_f64(vc), L.numpy(), scale)
+    assert _maxerr(o, want) <= 2e-2
+
+
+@pytest.mark.parametrize("split", [32, 64, 128, 256, 1024])
+def test_decode_gqa_ragged_lengths(attn, split):
+    lengths = [0, 1, 31, 32, 127, 128, 129, 500, 2055, 2056]
+    q, kc, vc, L = decode_gqa_inputs(len(lengths), 16, 4, 128, 2056, 0, "bf16", seed=split,
+                                     nan_tail=True, lengths=lengths)
+    o = attn.decode_gqa(*_dev(q, kc, vc, L), 0.1, split=split)
+    want = oracle.decode_gqa(to_f64(q), to_f64(kc), to_f64(vc), L.numpy(), 0.1)
+    assert _maxerr(o, want) <= 2e-2
+    assert torch.all(o[0].cpu() == 0)  # kv_len 0 -> zeros
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (16, 1), (12, 4)])
+def test_decode_gqa_group_sizes(attn, Hq, Hkv):
+    q, kc, vc, L = decode_gqa_inputs(3, Hq, Hkv, 128, 400, 0, "f16", seed=Hq, lengths=[400, 333, 7])
+    o = attn.decode_gqa(*_dev(q, kc, vc, L), 0.09)
+    want = oracle.decode_gqa(to_f64(q), to_f64(kc), to_f64(vc), L.numpy(), 0.09)
+    assert _maxerr(o, want) <= 2e-2
+
+
+def test_decode_equals_prefill_row_on_gpu(attn):
+    """decode at position t == row t of a causal prefill over the same K/V (both on the GPU)."""
+    S, scale = 512, 1 / math.sqrt(128)
+    q, k, v = prefill_inputs(2, 16, 4, S, 128, "bf16", seed=4)
+    qg, kg, vg = _dev(q, k, v)
+    full = attn.prefill_gqa_rope(qg, kg, vg, scale, causal=True).float()
+    for t in (0, 1, 127, 300, S - 1):
+        L = torch.full((2,), t + 1, dtype=torch.int32, device="cuda")
+        dec = attn.decode_gqa(qg[:, :, t].contiguous(), kg, vg, L, scale, split=64).float()
+        assert float((dec - full[:, :, t]).abs().max()) <= 2e-2
+
+
+def test_decode_gqa_hipgraph_replay(attn):
+    """Decode captured in a hipGraph replays to the eager result (lengths read from device)."""
+    q, kc, vc, L = _dev(*decode_gqa_inputs(8, 16, 4, 128, 2056, 2048, "bf16", seed=2))
+    ws = torch.empty(attn.decode_gqa_workspace_bytes(8, 16, 2056, 128, 128), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    eager = attn.decode_gqa(q, kc, vc, L, 0.088, split=128, workspace=ws).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        attn.decode_gqa(q, kc, vc, L, 0.088, split=128, out=out, workspace=ws)  # warm up on the side stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            attn.decode_gqa(q, kc, vc, L, 0.088, split=128, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        _ = (q.float() * 2).sum()  # unrelated eager work between replays
+    # a shorter length takes effect without re-capture
+    L.fill_(1000)
+    g.replay()
+    torch.cuda.synchronize()
+    want = attn.decode_gqa(q, kc, vc, L, 0.088, split=128)
+    assert torch.equal(out, want)
+
+
+# ----------------------------------------------------------------------------
+# MLA decode
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [1, 32, 128])
+def test_decode_mla_config(attn, B):
+    """Absorbed-MLA decode: H=16, latent 448 + rope 64, context 2048 in
+    capacity 2056, scale 1/sqrt(192), bf16; NaN in the unused slots."""
+    q, c, L = decode_mla_inputs(B, 16, 448, 64, 2056, 2048, "bf16", nan_tail=True)
+    scale = 1 / math.sqrt(192)
+    o = attn.decode_mla(*_dev(q, c, L), scale)
+    want = oracle.decode_mla(to_f64(q), to_f64(c), L.numpy(), scale, 448)
+    assert _maxerr(o, want) <= 2e-2
+
+
+@pytest.mark.parametrize("split", [32, 128, 256, 512, 2048])
+def test_decode_mla_ragged(attn, split):
+    lengths = [0, 1, 33, 256, 257, 2056]
+    q, c, L = decode_mla_inputs(len(lengths), 16, 448, 64, 2056, 0, "bf16", seed=split, nan_tail=True,
+                                lengths=lengths)
+    o = attn.decode_mla(*_dev(q, c, L), 0.072, split=split)
+    want = oracle.decode_mla(to_f64(q), to_f64(c), L.numpy(), 0.072, 448)
+    assert _maxerr(o, want) <= 2e-2
+    assert torch.all(o[0].cpu() == 0)
+
+
+def test_decode_mla_fewer_heads_f16(attn):
+    q, c, L = decode_mla_inputs(2, 5, 448, 64, 300, 0, "f16", seed=6, lengths=[300, 100])
+    o = attn.decode_mla(*_dev(q, c, L), 0.072)
+    want = oracle.decode_mla(to_f64(q), to_f64(c), L.numpy(), 0.072, 448)
+    assert _maxerr(o, want) <= 2e-2
+
+
+# ----------------------------------------------------------------------------
+# Combine on its own
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("D,ns,empty", [(128, 17, 0), (448, 9, 3), (64, 5, 1), (1000, 3, 2)])
+def test_combine_matches_pairwise_merge(attn, D, ns, empty):
+    o_part, lse = split_partials(40, ns, D, seed=D, empty_every=empty)
+    got = attn.combine_splits(*_dev(o_part, lse))
+    want = oracle.combine_splits(o_part.numpy(), lse.numpy())
+    assert _maxerr(got, want) <= 1e-5
