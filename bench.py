@@ -1,0 +1,259 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+A step is one causal GQA prefill with fused RoPE at the full workload
+(B=1, Hq=32, Hkv=8, S=2048, D=128, bf16 in and out, theta 10000): one launch
+of the prefill kernel.  ``value`` is its throughput in useful TFLOP/s
+(4 * B * Hq * D * S(S+1)/2 flops per step, masked work excluded), with inputs
+resident in HBM.  The same JSON line carries the roofline of that kernel, the
+CPU float64 oracle timed on a bounded sample of the same workload, and the
+other paths (GQA and MLA decode in eager and hipGraph modes, MHA forward in
+fp16 / fp8, the tiny fp32 prefill) as secondary figures.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOP/s (% MFMA peak); decode µs/step and HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(B, H, S, D, causal):
+    return 4.0 * B * H * D * (S * (S + 1) / 2 if causal else S * S)
+
+
+def gqa_decode_bytes(B, Hq=16, Hkv=4, D=128, L=2048, elem=2):
+    return B * (L * Hkv * D * 2 * elem + 2 * Hq * D * elem)
+
+
+def mla_decode_bytes(B, H=16, dq=512, dl=448, L=2048, elem=2):
+    return B * (L * dq * elem + H * dq * elem + H * dl * elem)
+
+
+def time_loop(fn, iters, warmup):
+    """Average ms per call of fn() over `iters` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def time_graph(fn, steps_per_graph, replays, warmup=2):
+    """ms per step with `steps_per_graph` calls captured in one hipGraph."""
+    import torch
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for _ in range(steps_per_graph):
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (replays * steps_per_graph)
+
+
+def cpu_baseline(budget_s=15.0):
+    """Time the float64 oracle on KV groups of the full prefill workload until
+    about `budget_s` seconds of CPU work (or the whole workload) is done."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    import oracle
+    from workloads import prefill_inputs, to_f64
+    q, k, v = prefill_inputs(1, 32, 8, 2048, 128, "bf16")
+    qd, kd, vd = to_f64(q), to_f64(k), to_f64(v)
+    scale = 1 / math.sqrt(128)
+    t0 = time.perf_counter()
+    groups = 0
+    for g in range(8):
+        oracle.prefill(qd[:, 4 * g:4 * g + 4], kd[:, g:g + 1], vd[:, g:g + 1], scale, True, 10000.0)
+        groups += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = prefill_flops(1, 4 * groups, 2048, 128, True)
+    del np
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{groups} of 8 KV groups ({4 * groups} of 32 query heads) of the causal GQA "
+                      f"RoPE prefill B=1 S=2048 D=128, float64 numpy, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="prefill step only (for profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        log("bench.py measures one GPU only: this build has no multi-GPU path "
+            "(the prefill shards by KV-head group and decode by batch with no exchange).")
+        sys.exit(2)
+
+    import torch
+    import attention_flash_attn_02_amd as attn
+    from workloads import decode_gqa_inputs, decode_mla_inputs, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    attn.lib()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---- the step: causal GQA prefill with fused RoPE, full workload ----
+    B, Hq, Hkv, S, D = 1, 32, 8, 2048, 128
+    q, k, v = [t.to(dev) for t in prefill_inputs(B, Hq, Hkv, S, D, "bf16")]
+    out = torch.empty_like(q)
+    scale = 1 / math.sqrt(D)
+
+    def step():
+        attn.prefill_gqa_rope(q, k, v, scale, causal=True, rope_theta=10000.0, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = prefill_flops(B, Hq, S, D, True)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"prefill gqa+rope bf16 S=2048: {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal GQA prefill with fused RoPE", "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "seq_len": S, "head_dim": D, "rope_theta": 10000.0,
+                   "in_dtype": "bf16", "out_dtype": "bf16", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_mfma_kernel<bf16,128,causal,rope>",
+                     "algorithmic_per_launch": flops},
+    }
+
+    if not args.quick:
+        sec = {}
+        # graph replay of the prefill step
+        ms_g = time_graph(step, 10, 10)
+        sec["prefill_gqa_rope_graph"] = {"us_per_step": round(ms_g * 1e3, 2),
+                                         "tflops": round(flops / (ms_g * 1e-3) / 1e12, 1)}
+        # tiny fp32 prefill
+        qt, kt, vt = [t.to(dev) for t in prefill_inputs(1, 4, 2, 128, 64, "f32")]
+        ms_t = time_loop(lambda: attn.prefill_gqa_rope(qt, kt, vt, 1 / 8, causal=True), 100, 10)
+        sec["prefill_tiny_f32"] = {"us_per_step": round(ms_t * 1e3, 2)}
+        # MHA forward Z=4, H=32, fp16 and fp8 e5m2 (fp16 out)
+        mha = {}
+        for D_, causal in ((64, False), (128, True)):
+            for N in (1024, 4096, 16384):
+                for dt in ("f16", "fp8_e5m2"):
+                    qm, km, vm = [t.to(dev) for t in prefill_inputs(4, 32, 32, N, D_, dt, seed=N)]
+                    om = torch.empty(qm.shape, dtype=torch.float16, device=dev)
+                    it = 20 if N <= 4096 else 5
+                    ms_m = time_loop(lambda: attn.prefill_gqa_rope(qm, km, vm, 1 / math.sqrt(D_), causal=causal,
+                                                                  out=om), it, 3)
+                    f = prefill_flops(4, 32, N, D_, causal)
+                    tf = f / (ms_m * 1e-3) / 1e12
+                    peak = PEAK_FP8_TFLOPS if dt == "fp8_e5m2" else PEAK_BF16_TFLOPS
+                    mha[f"D{D_}_{'causal' if causal else 'noncausal'}_N{N}_{dt}"] = {
+                        "us": round(ms_m * 1e3, 1), "tflops": round(tf, 1), "frac": round(tf / peak, 4)}
+                    del qm, km, vm, om
+        sec["mha_fwd_Z4_H32"] = mha
+        log("mha:", json.dumps(mha))
+        # GQA decode, split 128
+        dec = {}
+        for Bd in (1, 8, 32, 64, 128):
+            qd, kc, vc, L = [t.to(dev) for t in decode_gqa_inputs(Bd, 16, 4, 128, 2056, 2048, "bf16")]
+            od = torch.empty_like(qd)
+            ws = torch.empty(attn.decode_gqa_workspace_bytes(Bd, 16, 2056, 128, 128), dtype=torch.uint8, device=dev)
+            fn = lambda: attn.decode_gqa(qd, kc, vc, L, scale, split=128, out=od, workspace=ws)  # noqa: E731
+            me = time_loop(fn, 50, 5)
+            mg = time_graph(fn, 20, 5)
+            by = gqa_decode_bytes(Bd)
+            dec[f"B{Bd}"] = {"eager_us": round(me * 1e3, 2), "graph_us": round(mg * 1e3, 2),
+                             "graph_GBs": round(by / (mg * 1e-3) / 1e9, 1),
+                             "graph_frac": round(by / (mg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "eager_GBs": round(by / (me * 1e-3) / 1e9, 1), "bytes": by}
+            del qd, kc, vc, L, od, ws
+        sec["decode_gqa_split128"] = dec
+        log("decode gqa:", json.dumps(dec))
+        mla = {}
+        for Bd in (1, 32, 128):
+            qm, cm, L = [t.to(dev) for t in decode_mla_inputs(Bd, 16, 448, 64, 2056, 2048, "bf16")]
+            om = torch.empty((Bd, 16, 448), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(attn.decode_mla_workspace_bytes(Bd, 16, 2056, 448, 0), dtype=torch.uint8, device=dev)
+            fn = lambda: attn.decode_mla(qm, cm, L, 1 / math.sqrt(192), out=om, workspace=ws)  # noqa: E731
+            me = time_loop(fn, 50, 5)
+            mg = time_graph(fn, 20, 5)
+            by = mla_decode_bytes(Bd)
+            mla[f"B{Bd}"] = {"eager_us": round(me * 1e3, 2), "graph_us": round(mg * 1e3, 2),
+                             "graph_GBs": round(by / (mg * 1e-3) / 1e9, 1),
+                             "graph_frac": round(by / (mg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "eager_GBs": round(by / (me * 1e-3) / 1e9, 1), "bytes": by}
+            del qm, cm, L, om, ws
+        sec["decode_mla"] = mla
+        log("decode mla:", json.dumps(mla))
+        result["secondary"] = sec
+
+    if not args.no_cpu and not args.quick:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline()
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
