@@ -13,4 +13,5 @@ from .ops import (  # noqa: F401
     decode_mla,
     decode_mla_workspace_bytes,
     prefill_gqa_rope,
+    prefill_num_configs,
 )

@@ -46,6 +46,11 @@ struct Bf16Tag {
     r[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, r);
   }
+  // acc + lo + hi of a packed pair (v_dot2 with (1, 1))
+  __device__ static inline float sum2(uint32_t packed, float acc) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 v2;
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, packed), __builtin_bit_cast(v2, 0x3f803f80u), acc, false);
+  }
   __device__ static inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -67,6 +72,10 @@ struct F16Tag {
     r[0] = (_Float16)lo;
     r[1] = (_Float16)hi;
     return __builtin_bit_cast(uint32_t, r);
+  }
+  __device__ static inline float sum2(uint32_t packed, float acc) {
+    typedef __attribute__((ext_vector_type(2))) _Float16 v2;
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2, packed), __builtin_bit_cast(v2, 0x3c003c00u), acc, false);
   }
   __device__ static inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),

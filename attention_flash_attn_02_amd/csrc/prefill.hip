@@ -50,7 +50,13 @@ struct PrefillParams {
   int out_dtype;
   int rope;
   float inv_freq[64];  // RoPE inverse frequencies theta^(-2i/D), i < D/2
-  double rope_frev[64];  // the same frequencies in revolutions per position (/ 2 pi)
+  // RoPE frequencies in revolutions per position, f = theta^(-2i/D) / (2 pi),
+  // split as f_hi + f_lo with f_hi carrying 8 significant bits: pos * f_hi is
+  // then exact in fp32 for pos < 2^16, so frac(pos * f_hi) + pos * f_lo gives
+  // the angle modulo one revolution to ~1e-7 without fp64 arithmetic.
+  float rope_fhi[64];
+  float rope_flo[64];
+  int halves;  // MFMA kernel: 1 = 4-wave workgroups, 2 = 8-wave split-key workgroups
 };
 
 // ---------------------------------------------------------------------------
@@ -410,15 +416,19 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
 // one (items k and n-1-k of the longest-first order), so every workgroup has
 // the same amount of work.
 //
+// One workgroup barrier per key tile: after it, each half issues the loads of
+// its next tile into the other LDS stage and computes S^T = K Q^T, the online
+// softmax and O^T += V^T P^T for its current tile.  MFMA operands are read
+// from LDS a few MFMAs ahead of their use.
+//
 // K and V tiles go straight from HBM to LDS (global_load_lds, 16 B per lane)
-// into XOR-swizzled row-major layouts, double buffered, with one barrier per
-// key tile.  V is read transposed by ds_read_b64_tr_b16: each 16-lane group
-// reads a 4-key x 16-dim block and every lane receives one dim column of 4
-// keys, which is exactly the A operand of O^T = V^T P^T.  With RoPE the K
-// tile is instead loaded into registers, rotated and written to LDS.
-// The running row maximum is only moved when a row's new maximum exceeds it
-// by more than 2^8 (lazy rescaling; the result is exact, the probabilities
-// just stay below 256 in the meantime).
+// into XOR-swizzled row-major layouts, two stages per tensor per half.  V is
+// read transposed by ds_read_b64_tr_b16: each 16-lane group reads a 4-key x
+// 16-dim block and every lane receives one dim column of 4 keys, which is
+// exactly the A operand of O^T = V^T P^T.  With RoPE the K tile is loaded
+// into registers, rotated in a V-step and written to LDS.  The running row
+// maximum is only moved when a row's maximum exceeds it by more than 2^8
+// (lazy rescaling: exact, the probabilities just stay below 256).
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(4))) short v4i16;
 #define LDS_AS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
@@ -434,8 +444,8 @@ __device__ inline float pair_sum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <class Tag, int D, bool CAUSAL, bool ROPE>
-__global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) {
+template <class Tag, int D, bool CAUSAL, bool ROPE, int HALVES>
+__global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const PrefillParams p) {
   constexpr int BN = 64;
   constexpr int ROWB = D * 2;        // bytes per K/V row
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -443,24 +453,61 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   constexpr int RPI = 64 / CH;       // rows per wave-wide direct load
   constexpr int IPW = BN / RPI / 4;  // direct loads per wave per tile
   constexpr int NKK = D / 16, NDB = D / 32, HALF = D / 2, PAIRS = D / 64;
-  constexpr float kLazy = 8.f;       // rescale only when the max grows by > 2^8
+  constexpr float kLazy = 8.f;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * 2 * TILEB];  // [half][stage][K,V]
-  __shared__ float rope_base[2][2][ROPE ? D : 1];  // [half][slot][rev0 | freq]: see rope_base_fill
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[HALVES * 4 * TILEB];  // [half][K0 K1 V0 V1]
+  __shared__ float rope_base[2][2][ROPE ? D : 1];                          // [half][slot][rev0 | freq]
 
+  // XOR swizzles of the 16-byte chunks of a row, for a 64-bank LDS (one
+  // 256-byte bank line = one D=128 row or two D=64 rows):
+  //   K, read by 16 consecutive rows at one chunk: rows must hit 16 distinct
+  //   bank groups;  V, read transposed as 4 rows x 4 chunks per 32 lanes.
+  auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+  auto vswz = [](int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int half = wave >> 2, wq = wave & 3, htid = tid & 255;
+  const int half = HALVES == 2 ? wave >> 2 : 0, wq = wave & 3, htid = tid & 255;
   const int m = lane & 31, hh = lane >> 5;
+  const int g = lane >> 4, rr = lane & 15;
   uint8_t* hbuf = smem + half * (4 * TILEB);
+
+  // ---- lane-constant LDS offsets ----
+  // K A operand: row 32 nb + m (the swizzle depends on m only), logical chunk 2 kk + hh
+  int koff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = m * ROWB + 16 * ((2 * kk + hh) ^ kswz(m));
+  // V^T A operand via transposing reads: this lane addresses key
+  // 16 c + 4 (g >> 1) + (rr >> 2) (+ 8), dims 32 db + 16 (g & 1) + 4 (rr & 3) .. + 3
+  // (the swizzle only depends on key mod 4, which the offsets 16 c and 8 keep)
+  int voff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d = 32 * db + 16 * (g & 1) + 4 * (rr & 3);
+    const int key = 4 * (g >> 1) + (rr >> 2);
+    voff[db] = key * ROWB + 16 * ((d >> 3) ^ vswz(key)) + 2 * (d & 7);
+  }
+  // direct-load lane offsets (row inside the tile, swizzled source chunk)
+  int dk[IPW], dv[IPW];
+#pragma unroll
+  for (int u = 0; u < IPW; ++u) {
+    const int row = RPI * (wq * IPW + u) + lane / CH, phys = lane % CH;
+    dk[u] = row * ROWB + 16 * (phys ^ kswz(row));
+    dv[u] = row * ROWB + 16 * (phys ^ vswz(row));
+  }
 
   const int per_ptile = p.B * p.Hkv * p.n_hgroups;
   const int n_items = p.n_ptiles * per_ptile;
-  const int item_long = blockIdx.x;
-  const int item_short = n_items - 1 - (int)blockIdx.x;
-  const int n_my = (CAUSAL && item_short > item_long) ? 2 : 1;
-
-  // RoPE staging of K: row kr, chunk pairs (kj + 4u, kj + 4u + CH/2)
-  const int kr = htid >> 2, kj = htid & 3;
+  // causal, 8 waves: this workgroup takes long item k and short item n-1-k.
+  // 4 waves: one item; the second half of the grid takes the short items in
+  // reverse order, so that workgroups k and k + n/2 (which tend to share a CU
+  // when two workgroups fit per CU) carry complementary amounts of work.
+  const int half_items = (n_items + 1) / 2;
+  int item_long = blockIdx.x, item_short = n_items - 1 - (int)blockIdx.x;
+  if (HALVES == 1 && CAUSAL)
+    item_long = (int)blockIdx.x < half_items ? (int)blockIdx.x : n_items - 1 - ((int)blockIdx.x - half_items);
+  const int n_my = (HALVES == 2 && CAUSAL && item_short > item_long) ? 2 : 1;
+  // RoPE staging: row kr, chunk pairs (kj + 4u, + CH/2); 16 consecutive lanes
+  // take 16 rows at one chunk so the LDS writes hit 16 distinct bank groups
+  const int kr = (htid & 15) + 16 * (htid >> 6), kj = (htid >> 4) & 3;
 
 #pragma unroll 1
   for (int itn = 0; itn < n_my; ++itn) {
@@ -477,7 +524,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const int pw0 = p0 + (wq / p.GP) * 32;
     const int kend = CAUSAL ? min(p.S, p0 + p.P) : p.S;
     const int n_kt = (kend + BN - 1) / BN;
-    const int n_it = (n_kt + 1) >> 1;  // iterations; this half takes tile 2 i + half
+    const int n = (n_kt + HALVES - 1) / HALVES;  // local tiles per half: local i is tile HALVES i + half
     const int qpos = pw0 + m;
 
     // ---- Q fragments (B operand of S^T = K Q^T) ----
@@ -499,9 +546,9 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
             float r1[2], r2[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-              // angle in revolutions, reduced exactly in fp64; v_sin/v_cos take revolutions
-              const double rv = (double)qpos * p.rope_frev[16 * kk + 8 * hh + 2 * e + s];
-              const float rev = (float)(rv - floor(rv));
+              // angle in revolutions (v_sin/v_cos take revolutions)
+              const int fi = 16 * kk + 8 * hh + 2 * e + s;
+              const float rev = __builtin_amdgcn_fractf((float)qpos * p.rope_fhi[fi]) + (float)qpos * p.rope_flo[fi];
               const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
               const float x1 = Tag::to_f32(s ? (w1 >> 16) : (w1 & 0xffff));
               const float x2 = Tag::to_f32(s ? (w2 >> 16) : (w2 & 0xffff));
@@ -517,24 +564,33 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const size_t kv_row0 = ((size_t)b * p.Hkv + kvh) * p.S;
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k) + kv_row0 * ROWB;
     const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.v) + kv_row0 * ROWB;
+    auto exists = [&](int i) { return i >= 0 && i < n && HALVES * i + half < n_kt; };
+    auto kbuf = [&](int i) { return hbuf + (i & 1) * TILEB; };
+    auto vbuf = [&](int i) { return hbuf + (2 + (i & 1)) * TILEB; };
 
-    // direct HBM -> LDS load of one K or V tile (rows past S re-read row S-1;
-    // those keys are masked and their probabilities are exactly zero)
-    auto dma_tile = [&](const uint8_t* src, uint8_t* dst, int key0, bool is_v) {
+    // direct HBM -> LDS load of local tile i of K or V (rows past S re-read
+    // row S-1: those keys are masked and their probabilities are exactly 0)
+    auto dma = [&](const uint8_t* src, uint8_t* dst, const int* loff, int i, bool is_v) {
+      const int key0 = (HALVES * i + half) * BN;
+      if (key0 + BN <= p.S) {
+        const uint8_t* base = src + (size_t)key0 * ROWB;
 #pragma unroll
-      for (int u = 0; u < IPW; ++u) {
-        const int row0 = RPI * (wq * IPW + u);
-        const int row = row0 + lane / CH;
-        const int phys = lane % CH;
-        const int swz = is_v ? 2 * (row & 3) : (row & 7);
-        const int key = min(key0 + row, p.S - 1);
-        __builtin_amdgcn_global_load_lds(src + (size_t)key * ROWB + 16 * (phys ^ swz),
-                                         LDS_AS(void, dst + row0 * ROWB), 16, 0, 0);
+        for (int u = 0; u < IPW; ++u)
+          __builtin_amdgcn_global_load_lds(base + loff[u], LDS_AS(void, dst + RPI * (wq * IPW + u) * ROWB), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+          const int row = RPI * (wq * IPW + u) + lane / CH, phys = lane % CH;
+          const int swz = is_v ? vswz(row) : kswz(row);
+          const int key = min(key0 + row, p.S - 1);
+          __builtin_amdgcn_global_load_lds(src + (size_t)key * ROWB + 16 * (phys ^ swz),
+                                           LDS_AS(void, dst + RPI * (wq * IPW + u) * ROWB), 16, 0, 0);
+        }
       }
     };
     u32x4 kreg[ROPE ? 2 * PAIRS : 1];
-    auto load_k_regs = [&](int key0) {
-      const int key = min(key0 + kr, p.S - 1);
+    auto load_k_regs = [&](int i) {
+      const int key = min((HALVES * i + half) * BN + kr, p.S - 1);
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) {
         const int c = kj + 4 * u;
@@ -542,17 +598,17 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
         kreg[2 * u + 1] = ldg16(kg + (size_t)key * ROWB + 16 * (c + CH / 2));
       }
     };
-    // angle of (position t*BN + r, frequency i) in revolutions:
-    //   frac(t*BN*f_i) + r*f_i, f_i = theta^(-2i/D) / (2 pi); the fraction of the
-    //   tile's base angle is taken in fp64 so that it stays exact at long contexts
-    auto rope_base_fill = [&](int t, int slot) {
+    // RoPE angle of (position key0 + r, frequency j) in revolutions:
+    //   [frac(key0 f_hi) + key0 f_lo] + r (f_hi + f_lo); the bracket is per tile
+    auto rope_base_fill = [&](int i) {
       if (wq == 0 && lane < HALF) {
-        const double rev = (double)(t * BN) * p.rope_frev[lane];
-        rope_base[half][slot][lane] = (float)(rev - floor(rev));
-        rope_base[half][slot][HALF + lane] = (float)p.rope_frev[lane];
+        const float key0 = (float)((HALVES * i + half) * BN);
+        rope_base[half][i & 1][lane] = __builtin_amdgcn_fractf(key0 * p.rope_fhi[lane]) + key0 * p.rope_flo[lane];
+        rope_base[half][i & 1][HALF + lane] = p.rope_fhi[lane] + p.rope_flo[lane];
       }
     };
-    auto rotate_store_k = [&](uint8_t* dst, int slot) {
+    auto rotate_store_k = [&](int i) {
+      uint8_t* dst = kbuf(i);
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) {
         const int c = kj + 4 * u;
@@ -562,11 +618,9 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
           float r1[2], r2[2];
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            const int i = 8 * c + 2 * e + s;
-            // revolutions in [0, 1 + 64 f_i): v_sin/v_cos take revolutions directly
-            const float rev = fmaf((float)kr, rope_base[half][slot][HALF + i], rope_base[half][slot][i]);
-            const float cs = __builtin_amdgcn_cosf(rev);
-            const float sn = __builtin_amdgcn_sinf(rev);
+            const int j = 8 * c + 2 * e + s;
+            const float rev = fmaf((float)kr, rope_base[half][i & 1][HALF + j], rope_base[half][i & 1][j]);
+            const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
             const float x1 = Tag::to_f32(s ? (lo[e] >> 16) : (lo[e] & 0xffff));
             const float x2 = Tag::to_f32(s ? (hi[e] >> 16) : (hi[e] & 0xffff));
             r1[s] = x1 * cs - x2 * sn;
@@ -575,65 +629,79 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
           lo[e] = Tag::pack2(r1[0], r1[1]);
           hi[e] = Tag::pack2(r2[0], r2[1]);
         }
-        *reinterpret_cast<u32x4*>(dst + kr * ROWB + 16 * (c ^ (kr & 7))) = lo;
-        *reinterpret_cast<u32x4*>(dst + kr * ROWB + 16 * ((c + CH / 2) ^ (kr & 7))) = hi;
+        *reinterpret_cast<u32x4*>(dst + kr * ROWB + 16 * (c ^ kswz(kr))) = lo;
+        *reinterpret_cast<u32x4*>(dst + kr * ROWB + 16 * ((c + CH / 2) ^ kswz(kr))) = hi;
       }
     };
+    auto active = [&](int i) {
+      return exists(i) && !(CAUSAL && (HALVES * i + half) * BN > pw0 + 31);
+    };
 
-    // ---- prologue: tile t(0) = half into stage 0 ----
-    if (half < n_kt) {
-      dma_tile(vg, hbuf + TILEB, half * BN, true);
-      if (ROPE) load_k_regs(half * BN);
-      else dma_tile(kg, hbuf, half * BN, false);
-    }
-    if (ROPE) {
-      rope_base_fill(half, 0);
-      rope_base_fill(half + 2, 1);
-      __syncthreads();
-      if (half < n_kt) rotate_store_k(hbuf, 0);
-    }
-
+    // ---- running state ----
     f32x16 acc_o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-    float m_ref = kNegInf;  // exponent reference (scaled log2 domain), same in both lanes of a row
+    float m_ref = kNegInf;  // exponent reference (scaled log2 domain), equal in both lanes of a row
     float l_run = 0.f;      // sum over this lane's keys of exp2(s - m_ref)
 
-#pragma unroll 1
-    for (int i = 0; i < n_it; ++i) {
-      const int t = 2 * i + half;
-      const int st = i & 1;
-      __builtin_amdgcn_s_waitcnt(0x3f70);  // this thread's direct loads have landed (vmcnt 0)
-      __syncthreads();
-      const int tn = t + 2;
-      const bool has_next = (i + 1 < n_it) && (tn < n_kt);
-      if (has_next) {
-        dma_tile(vg, hbuf + ((st ^ 1) * 2 + 1) * TILEB, tn * BN, true);
-        if (ROPE) load_k_regs(tn * BN);
-        else dma_tile(kg, hbuf + (st ^ 1) * 2 * TILEB, tn * BN, false);
+    // ---- prologue: local tile 0 into stage 0 ----
+    if (ROPE) {
+      rope_base_fill(0);
+      rope_base_fill(1);
+      if (exists(0)) {
+        dma(vg, vbuf(0), dv, 0, true);
+        load_k_regs(0);
       }
-      if (ROPE && i + 2 < n_it) rope_base_fill(t + 4, st);
+      __syncthreads();
+      if (exists(0)) rotate_store_k(0);
+    } else if (exists(0)) {
+      dma(kg, kbuf(0), dk, 0, false);
+      dma(vg, vbuf(0), dv, 0, true);
+    }
 
-      const int key0 = t * BN;
-      const bool active = (t < n_kt) && !(CAUSAL && key0 > pw0 + 31);
-      if (active) {
-        const uint8_t* kb = hbuf + st * 2 * TILEB;
-        const uint8_t* vb = kb + TILEB;
-        // ---- S^T = K Q^T ----
+#pragma unroll 1
+    for (int i = 0; i < n; ++i) {
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // this thread's loads of tile i have landed
+      __syncthreads();                     // ... and everybody's; stage (i+1)&1 is free
+      const bool has_next = exists(i + 1);
+      if (has_next) {
+        dma(vg, vbuf(i + 1), dv, i + 1, true);
+        if (ROPE) load_k_regs(i + 1);
+        else dma(kg, kbuf(i + 1), dk, i + 1, false);
+      }
+      if (ROPE) rope_base_fill(i + 2);
+
+      if (active(i)) {
+        // ---- S^T = K Q^T; A operands read from LDS three MFMAs ahead ----
         f32x16 acc_s[2];
+        {
+          const uint8_t* kb = kbuf(i);
+          constexpr int NJ = 2 * NKK;  // MFMA j = NKK nb + kk
+          auto rd = [&](int j) {
+            return *reinterpret_cast<const u32x4*>(kb + koff[j % NKK] + 32 * (j / NKK) * ROWB);
+          };
+          acc_s[0] = f32x16{};
+          acc_s[1] = f32x16{};
+          u32x4 fa[4];
+          fa[0] = rd(0);
+          fa[1] = rd(1);
+          fa[2] = rd(2);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          acc_s[nb] = f32x16{};
-          const int row = 32 * nb + m;
-          const uint8_t* krow = kb + row * ROWB;
-#pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * kk + hh) ^ (row & 7)));
+          for (int j = 0; j < NJ; ++j) {
+            if (j + 3 < NJ) fa[(j + 3) % 4] = rd(j + 3);
+            const int kk = j % NKK;
             const u32x4 bq = {qf[4 * kk], qf[4 * kk + 1], qf[4 * kk + 2], qf[4 * kk + 3]};
-            acc_s[nb] = Tag::mfma32(a, bq, acc_s[nb]);
+            acc_s[j / NKK] = Tag::mfma32(fa[j % 4], bq, acc_s[j / NKK]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            if (j + 3 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
           }
         }
         // ---- mask, lazy online softmax ----
+        const int key0 = (HALVES * i + half) * BN;
         const bool need_mask = (key0 + BN > p.S) || (CAUSAL && key0 + BN - 1 > pw0);
         if (need_mask) {
           // key = key0 + 4 hh + off(nb, r) is visible iff key <= min(qpos, S - 1)
@@ -660,45 +728,52 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
         }
         const float m_use = m_ref == kNegInf ? 0.f : m_ref;
         uint32_t pf[4][4];
-        float psum = 0.f;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
             const float e0 = fast_exp2(fmaf(acc_s[nb][r], p.scale_log2, -m_use));
             const float e1 = fast_exp2(fmaf(acc_s[nb][r + 1], p.scale_log2, -m_use));
-            psum += e0 + e1;
-            pf[2 * nb + (r >> 3)][(r & 7) >> 1] = Tag::pack2(e0, e1);
+            const uint32_t pk = Tag::pack2(e0, e1);
+            pf[2 * nb + (r >> 3)][(r & 7) >> 1] = pk;
+            l_run = Tag::sum2(pk, l_run);  // row sum of the rounded probabilities
           }
-        l_run += psum;
-        // ---- O^T += V^T P^T (V^T via transposing LDS reads) ----
-        const int g = lane >> 4, rr = lane & 15;
+        // ---- O^T += V^T P^T; transposing reads issued two MFMAs ahead ----
+        {
+          const uint8_t* vb = vbuf(i);
+          constexpr int NJ = NDB * 4;  // MFMA j = 4 db + c
+          auto rd = [&](int j) {
+            const int db = j >> 2, c = j & 3;
+            const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16, vb + voff[db] + 16 * c * ROWB));
+            const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16, vb + voff[db] + (16 * c + 8) * ROWB));
+            const u32x2 a1 = __builtin_bit_cast(u32x2, x1), a2 = __builtin_bit_cast(u32x2, x2);
+            return u32x4{a1[0], a1[1], a2[0], a2[1]};
+          };
+          u32x4 fa[3];
+          fa[0] = rd(0);
+          fa[1] = rd(1);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = 32 * db + 16 * (g & 1) + 4 * (rr & 3);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int tok1 = 16 * c + 4 * (g >> 1) + (rr >> 2), tok2 = tok1 + 8;
-            const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16,
-                vb + tok1 * ROWB + 16 * ((d >> 3) ^ (2 * (tok1 & 3))) + 2 * (d & 7)));
-            const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16,
-                vb + tok2 * ROWB + 16 * ((d >> 3) ^ (2 * (tok2 & 3))) + 2 * (d & 7)));
-            const u32x4 a = {(uint32_t)(uint16_t)x1[0] | ((uint32_t)(uint16_t)x1[1] << 16),
-                             (uint32_t)(uint16_t)x1[2] | ((uint32_t)(uint16_t)x1[3] << 16),
-                             (uint32_t)(uint16_t)x2[0] | ((uint32_t)(uint16_t)x2[1] << 16),
-                             (uint32_t)(uint16_t)x2[2] | ((uint32_t)(uint16_t)x2[3] << 16)};
+          for (int j = 0; j < NJ; ++j) {
+            if (j + 2 < NJ) fa[(j + 2) % 3] = rd(j + 2);
+            const int c = j & 3;
             const u32x4 bp = {pf[c][0], pf[c][1], pf[c][2], pf[c][3]};
-            acc_o[db] = Tag::mfma32(a, bp, acc_o[db]);
+            acc_o[j >> 2] = Tag::mfma32(fa[j % 3], bp, acc_o[j >> 2]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
         }
       }
-      if (ROPE && has_next) rotate_store_k(hbuf + (st ^ 1) * 2 * TILEB, (st ^ 1));
+      if (ROPE && has_next) rotate_store_k(i + 1);
     }
 
     // ---- merge the two halves (same rows, disjoint key tiles) ----
-    __syncthreads();
     float* sc = reinterpret_cast<float*>(smem) + wq * (NDB * 16 + 2) * 64;
-    if (half == 1) {
+    if (HALVES == 2) __syncthreads();
+    if (HALVES == 2 && half == 1) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -706,9 +781,10 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       sc[(NDB * 16) * 64 + lane] = m_ref;
       sc[(NDB * 16 + 1) * 64 + lane] = l_run;
     }
-    __syncthreads();
+    if (HALVES == 2) __syncthreads();
     if (half == 0) {
-      const float m1 = sc[(NDB * 16) * 64 + lane], l1 = sc[(NDB * 16 + 1) * 64 + lane];
+      const float m1 = HALVES == 2 ? sc[(NDB * 16) * 64 + lane] : kNegInf;
+      const float l1 = HALVES == 2 ? sc[(NDB * 16 + 1) * 64 + lane] : 0.f;
       const float M = fmaxf(m_ref, m1);
       const float Mu = M == kNegInf ? 0.f : M;
       const float f0 = fast_exp2(m_ref - Mu), f1 = fast_exp2(m1 - Mu);
@@ -724,7 +800,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g4 + e;
-              v4[e] = (acc_o[db][r] * f0 + sc[(db * 16 + r) * 64 + lane] * f1) * inv;
+              v4[e] = (HALVES == 2 ? acc_o[db][r] * f0 + sc[(db * 16 + r) * 64 + lane] * f1 : acc_o[db][r]) * inv;
             }
             store4(p.o, obase + 32 * db + 8 * g4 + 4 * hh, p.out_dtype, v4[0], v4[1], v4[2], v4[3]);
           }
@@ -825,17 +901,23 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
 // ---------------------------------------------------------------------------
 // Host dispatch
 // ---------------------------------------------------------------------------
-template <class Tag, int D>
-static void launch_v2(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
+template <class Tag, int D, int H>
+static void launch_fwd_h(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
   const long long items = (long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups;
-  const dim3 grid((unsigned)(causal ? (items + 1) / 2 : items));
+  const dim3 grid((unsigned)(causal && H == 2 ? (items + 1) / 2 : items)), block(256 * H);
   if (causal) {
-    if (rope) hipLaunchKernelGGL((prefill_v2_kernel<Tag, D, true, true>), grid, dim3(512), 0, st, p);
-    else hipLaunchKernelGGL((prefill_v2_kernel<Tag, D, true, false>), grid, dim3(512), 0, st, p);
+    if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, true, H>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, false, H>), grid, block, 0, st, p);
   } else {
-    if (rope) hipLaunchKernelGGL((prefill_v2_kernel<Tag, D, false, true>), grid, dim3(512), 0, st, p);
-    else hipLaunchKernelGGL((prefill_v2_kernel<Tag, D, false, false>), grid, dim3(512), 0, st, p);
+    if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, true, H>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, false, H>), grid, block, 0, st, p);
   }
+}
+
+template <class Tag, int D>
+static void launch_fwd(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
+  if (p.halves == 1) launch_fwd_h<Tag, D, 1>(p, causal, rope, st);
+  else launch_fwd_h<Tag, D, 2>(p, causal, rope, st);
 }
 
 template <class Tag, int D, bool FP8>
@@ -860,12 +942,11 @@ static void launch_f32(const PrefillParams& p, bool causal, bool rope, hipStream
 
 using namespace attn;
 
-extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, void* o,
-                                             float* lse, int B, int Hq, int Hkv, int S, int D,
-                                             attn_dtype in_dtype, attn_dtype out_dtype,
-                                             float softmax_scale, int causal, float rope_theta,
-                                             float q_descale, float k_descale, float v_descale,
-                                             hipStream_t stream) {
+static attn_status prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int S, int D, attn_dtype in_dtype,
+                                attn_dtype out_dtype, float softmax_scale, int causal,
+                                float rope_theta, float q_descale, float k_descale,
+                                float v_descale, int config, hipStream_t stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -892,10 +973,17 @@ extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const
   p.out_scale = v_descale;
   p.out_dtype = out_dtype;
   p.rope = rope ? 1 : 0;
+  p.halves = config == 1 ? 2 : 1;
+  if (rope && S > 65536) return ATTN_ERR_UNSUPPORTED;  // exact angle reduction needs pos < 2^16
   for (int i = 0; i < D / 2; ++i) {
     const double w = rope ? pow((double)rope_theta, -2.0 * i / D) : 0.0;
+    const double f = w / (2.0 * 3.14159265358979323846);
+    int ex = 0;
+    const double mant = frexp(f, &ex);               // f = mant * 2^ex, mant in [0.5, 1)
+    const double hi = ldexp(floor(ldexp(mant, 8)), ex - 8);  // 8 significant bits
     p.inv_freq[i] = (float)w;
-    p.rope_frev[i] = w / (2.0 * 3.14159265358979323846);
+    p.rope_fhi[i] = (float)hi;
+    p.rope_flo[i] = (float)(f - hi);
   }
 
   if (in_dtype == ATTN_F32) {
@@ -917,12 +1005,12 @@ extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const
   const bool c = causal != 0;
   switch (in_dtype) {
     case ATTN_BF16:
-      if (D == 64) launch_v2<Bf16Tag, 64>(p, c, rope, stream);
-      else launch_v2<Bf16Tag, 128>(p, c, rope, stream);
+      if (D == 64) launch_fwd<Bf16Tag, 64>(p, c, rope, stream);
+      else launch_fwd<Bf16Tag, 128>(p, c, rope, stream);
       break;
     case ATTN_F16:
-      if (D == 64) launch_v2<F16Tag, 64>(p, c, rope, stream);
-      else launch_v2<F16Tag, 128>(p, c, rope, stream);
+      if (D == 64) launch_fwd<F16Tag, 64>(p, c, rope, stream);
+      else launch_fwd<F16Tag, 128>(p, c, rope, stream);
       break;
     default:  // fp8 e5m2 (RoPE rejected above)
       if (D == 64) launch_mfma<F16Tag, 64, true>(p, c, grid, stream);
@@ -931,3 +1019,31 @@ extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const
   }
   return attn_host::launch_status();
 }
+
+// Tile configurations of the 16-bit MFMA prefill kernel (fp32 and fp8 inputs
+// have a single configuration):
+//   0 (global default): 4-wave workgroups, 128 query rows, 64-key tiles;
+//   1: 8-wave workgroups whose two halves split the key tiles of 128 rows.
+static const int kPrefillConfigs = 2;
+
+extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, void* o,
+                                             float* lse, int B, int Hq, int Hkv, int S, int D,
+                                             attn_dtype in_dtype, attn_dtype out_dtype,
+                                             float softmax_scale, int causal, float rope_theta,
+                                             float q_descale, float k_descale, float v_descale,
+                                             hipStream_t stream) {
+  return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, in_dtype, out_dtype, softmax_scale, causal,
+                      rope_theta, q_descale, k_descale, v_descale, 0, stream);
+}
+
+extern "C" attn_status attn_prefill_gqa_rope_with_config(
+    const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,
+    int D, attn_dtype in_dtype, attn_dtype out_dtype, float softmax_scale, int causal,
+    float rope_theta, float q_descale, float k_descale, float v_descale, int config,
+    hipStream_t stream) {
+  if (config < 0 || config >= kPrefillConfigs) return ATTN_ERR_UNSUPPORTED;
+  return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, in_dtype, out_dtype, softmax_scale, causal,
+                      rope_theta, q_descale, k_descale, v_descale, config, stream);
+}
+
+extern "C" int attn_prefill_num_configs(void) { return kPrefillConfigs; }

@@ -35,10 +35,15 @@ def _stream(stream) -> int:
     return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
 
 
+def prefill_num_configs() -> int:
+    return int(_lib.lib().attn_prefill_num_configs())
+
+
 def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_theta: float = 0.0,
                      out_dtype=None, out=None, return_lse: bool = False, q_descale: float = 1.0,
-                     k_descale: float = 1.0, v_descale: float = 1.0, stream=None):
-    """attn_prefill_gqa_rope: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> o [B,Hq,S,D] (and lse [B,Hq,S])."""
+                     k_descale: float = 1.0, v_descale: float = 1.0, stream=None, config=None):
+    """attn_prefill_gqa_rope: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> o [B,Hq,S,D] (and lse [B,Hq,S]).
+    ``config`` selects a tile configuration (attn_prefill_gqa_rope_with_config); None = global."""
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
@@ -50,10 +55,13 @@ def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_th
     if out is None:
         out = torch.empty((B, Hq, S, D), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if return_lse else None
-    code = _lib.lib().attn_prefill_gqa_rope(
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
-        B, Hq, Hkv, S, D, _dtype_code(q), _dtype_code(out), float(softmax_scale), int(bool(causal)),
-        float(rope_theta), float(q_descale), float(k_descale), float(v_descale), _stream(stream))
+    args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
+            B, Hq, Hkv, S, D, _dtype_code(q), _dtype_code(out), float(softmax_scale), int(bool(causal)),
+            float(rope_theta), float(q_descale), float(k_descale), float(v_descale)]
+    if config is None:
+        code = _lib.lib().attn_prefill_gqa_rope(*args, _stream(stream))
+    else:
+        code = _lib.lib().attn_prefill_gqa_rope_with_config(*args, int(config), _stream(stream))
     _lib.check(code)
     return (out, lse) if return_lse else out
 

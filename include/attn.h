@@ -82,7 +82,9 @@ const char* attn_status_str(attn_status s);
  *
  * in_dtype: ATTN_F32, ATTN_F16, ATTN_BF16 or ATTN_FP8_E5M2.
  * out_dtype: ATTN_F32, ATTN_F16 or ATTN_BF16.  D: 64 or 128.
- * rope_theta <= 0 disables RoPE (RoPE with fp8 input: ATTN_ERR_UNSUPPORTED).
+ * rope_theta <= 0 disables RoPE (RoPE with fp8 input, or with S > 65536:
+ * ATTN_ERR_UNSUPPORTED).  softmax_scale * q_descale * k_descale must be a
+ * positive finite number (ATTN_ERR_SHAPE otherwise).
  * q_descale, k_descale multiply the scores and v_descale the output (per-
  * tensor dequantisation factors; pass 1.0 for unscaled inputs).
  * Math is fp32 with fp32 accumulation; 16-bit and fp8 inputs use MFMA.
@@ -93,6 +95,24 @@ attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, v
                                   float softmax_scale, int causal, float rope_theta,
                                   float q_descale, float k_descale, float v_descale,
                                   hipStream_t stream);
+
+/* Tile-configuration sweep: the same prefill with an explicit configuration
+ * id in [0, attn_prefill_num_configs()).  Configuration 0 is the one global
+ * configuration attn_prefill_gqa_rope uses; the others exist so that a
+ * per-shape sweep can measure how far the global choice is from the best
+ * configuration of each shape (the shape-adaptive attention lesson page,
+ * row "Actual result": the global candidate's gap to the per-invocation
+ * oracle).  For the 16-bit MFMA kernel: 0 = 4-wave workgroups of 128 query
+ * rows; 1 = 8-wave workgroups whose halves split the key tiles of 128 rows.
+ * fp32 and fp8 inputs ignore the id (one configuration).  An id out of range
+ * returns ATTN_ERR_UNSUPPORTED. */
+int attn_prefill_num_configs(void);
+attn_status attn_prefill_gqa_rope_with_config(const void* q, const void* k, const void* v, void* o,
+                                              float* lse, int B, int Hq, int Hkv, int S, int D,
+                                              attn_dtype in_dtype, attn_dtype out_dtype,
+                                              float softmax_scale, int causal, float rope_theta,
+                                              float q_descale, float k_descale, float v_descale,
+                                              int config, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Split-context GQA decode ("flash-decoding"): one new query token per

@@ -67,6 +67,36 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S):
     assert _maxerr(lse, want_lse) <= 2e-2
 
 
+@pytest.mark.parametrize("config", [0, 1])
+@pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
+                                                  (128, False, True, "f16"), (64, True, True, "bf16")])
+def test_prefill_every_tile_config(attn, config, D, causal, rope, dtype):
+    """Every tile configuration of the sweep passes parity before it is timed."""
+    assert attn.prefill_num_configs() == 2
+    q, k, v = prefill_inputs(2, 8, 2, 333, D, dtype, seed=config * 7 + D)
+    theta = 10000.0 if rope else 0.0
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta, config=config)
+    want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta)
+    assert _maxerr(o, want) <= TOL[dtype]
+
+
+def test_prefill_config_out_of_range(attn):
+    q, k, v = _dev(*prefill_inputs(1, 2, 2, 16, 64, "bf16"))
+    with pytest.raises(attn.AttnError):
+        attn.prefill_gqa_rope(q, k, v, 0.125, config=2)
+
+
+def test_prefill_rope_long_positions(attn):
+    """RoPE angles stay exact at long contexts: sampled rows near position 16383."""
+    q, k, v = prefill_inputs(1, 2, 1, 16384, 128, "f16", seed=77)
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.088, causal=True, rope_theta=10000.0).cpu()
+    rows = [0, 8191, 16000, 16383]
+    for h in range(2):
+        want, _ = oracle.prefill_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(), 0.088, True,
+                                      10000.0, 0, h, rows)
+        assert _maxerr(o[0, h, rows], want) <= 2e-2
+
+
 @pytest.mark.parametrize("S", [1, 2, 31, 32, 33, 64, 65])
 def test_prefill_short_sequences(attn, S):
     q, k, v = prefill_inputs(1, 8, 2, S, 128, "bf16", seed=S)
