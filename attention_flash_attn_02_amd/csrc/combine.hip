@@ -15,40 +15,59 @@
 
 namespace attn {
 
-__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o_part,
-                                                     const float* __restrict__ lse_part,
-                                                     void* __restrict__ o, int nsplit, int D,
-                                                     int out_dtype) {
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x;
+// One wave per row; four rows per workgroup.  Lane s holds split s's weight
+// (splits beyond 64 are folded in a loop), the weights are broadcast with
+// readlane, and the partial rows are read with independent loads.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part,
+                                                      void* __restrict__ o, int R, int nsplit, int D,
+                                                      int out_dtype) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= R) return;
   const float* lse = lse_part + (size_t)r * nsplit;
   float mx = kNegInf;
-  for (int s = tid; s < nsplit; s += 64) mx = fmaxf(mx, lse[s]);
+  for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, lse[s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   const size_t obase = (size_t)r * D;
   if (mx == kNegInf) {
-    for (int d = tid; d < D; d += 64) store1(o, obase + d, out_dtype, 0.f);
+    for (int d = lane; d < D; d += 64) store1(o, obase + d, out_dtype, 0.f);
     return;
   }
   float wsum = 0.f;
-  for (int s = 0; s < nsplit; ++s) wsum += fast_exp2((lse[s] - mx) * kLog2e);
+  for (int s = lane; s < nsplit; s += 64) wsum += fast_exp2((lse[s] - mx) * kLog2e);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
   const float inv = 1.f / wsum;
   const float* op = o_part + (size_t)r * nsplit * D;
-  for (int d = tid; d < D; d += 64) {
+  for (int d0 = 0; d0 < D; d0 += 64) {
+    const int d = d0 + lane;
     float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float w = fast_exp2((lse[s] - mx) * kLog2e);
-      acc = fmaf(w, op[(size_t)s * D + d], acc);
+    for (int s0 = 0; s0 < nsplit; s0 += 64) {
+      const float w_l = s0 + lane < nsplit ? fast_exp2((lse[s0 + lane] - mx) * kLog2e) : 0.f;
+      const int ns = min(64, nsplit - s0);
+      int s = 0;
+      for (; s + 4 <= ns; s += 4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = d < D ? op[(size_t)(s0 + s + u) * D + d] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = fmaf(__shfl(w_l, s + u), v[u], acc);
+      }
+      for (; s < ns; ++s) {
+        const float v = d < D ? op[(size_t)(s0 + s) * D + d] : 0.f;
+        acc = fmaf(__shfl(w_l, s), v, acc);
+      }
     }
-    store1(o, obase + d, out_dtype, acc * inv);
+    if (d < D) store1(o, obase + d, out_dtype, acc * inv);
   }
 }
 
 void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
                     int out_dtype, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(R), dim3(64), 0, stream, o_part, lse_part, o, nsplit, D,
-                     out_dtype);
+  hipLaunchKernelGGL(combine_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, o_part, lse_part, o, R,
+                     nsplit, D, out_dtype);
 }
 
 }  // namespace attn

@@ -8,18 +8,8 @@
 // tile carries few useful query rows; here they ride in the 16-wide N side
 // of a 16x16x32 MFMA).
 //
-// Kernel 1 (this file): one workgroup per (split, KV head, sequence); each
-// wave takes 32-slot chunks of the split:
-//   * K rows go straight from HBM into registers as the A operand of
-//     S^T = K Q^T (16 B per lane per load, whole 256-B rows per 16 lanes);
-//   * V rows are loaded with whole-row coalescing, transposed in registers
-//     and written to the wave's own LDS area as V^T, whose slot order inside
-//     each 32-slot chunk matches the score accumulator, so O^T += V^T P^T
-//     takes its A operand as one 16-byte LDS read;
-//   * per-wave online softmax; the waves' partials are merged through LDS and
-//     one (o, lse) partial per query head and split is written to the
-//     workspace.
-// Kernel 2 (combine.hip) merges the splits.
+// Kernel 1 (this file) computes one (o, lse) partial per query head and
+// split; kernel 2 (combine.hip) merges the splits.
 // Slots at or past kv_len are never loaded; a split that starts past kv_len
 // writes the empty partial (o = 0, lse = -inf).
 
@@ -39,69 +29,98 @@ struct DecodeGqaParams {
   float scale_log2;
 };
 
-template <class Tag, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void decode_gqa_split_kernel(const DecodeGqaParams p) {
+typedef __attribute__((ext_vector_type(4))) short v4i16_t;
+#define LDS_PTR(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+
+// Streaming 16-byte load (non-temporal: the cache rows are read exactly once).
+__device__ inline u32x4 ldg16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// One wave per (split, KV head, sequence).  The split is walked in chunks of
+// 32 slots; the next chunk's K and V rows are loaded (16 B per lane, into a
+// second register set) while the current chunk is computed, so loads stay in
+// flight the whole time:
+//   * K rows are the A operand of S^T = K Q^T straight from registers;
+//   * V rows are stored row-major in this wave's LDS area (chunk swizzle
+//     2 (row & 7)) and read back transposed with ds_read_b64_tr_b16, which
+//     yields the A operand of O^T = V^T P^T directly.
+// The partial (normalised o, lse) of the split is written to the workspace.
+template <class Tag>
+__global__ __launch_bounds__(64) void decode_gqa_split_kernel(const DecodeGqaParams p) {
   constexpr int D = 128;
+  constexpr int ROWB = 2 * D;  // bytes per cache row
   constexpr int NDB = D / 16;  // 16-row blocks of O^T
   constexpr int NKK = D / 32;  // 32-wide k-steps of S^T
-  constexpr int VP = 32 + 8;   // V^T row pitch in 16-bit elements
-  __shared__ __attribute__((aligned(16))) uint16_t vt[WAVES][D * VP];
-  __shared__ float red_m[WAVES][16];
-  __shared__ float red_l[WAVES][16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs[32 * ROWB];  // V rows of the chunk
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x;
   const int m16 = lane & 15, qq = lane >> 4;
   const int split_idx = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int L = min(max(p.kv_len[b], 0), p.cap);
   const int s0 = split_idx * p.split;
   const int s1 = min(s0 + p.split, L);
-  const int row0 = b * p.Hq + kvh * p.G;  // first output row (query head) of this KV head
+  const int row0 = b * p.Hq + kvh * p.G;  // first query head (output row) of this KV head
 
   if (s0 >= s1) {  // empty split
-    for (int idx = tid; idx < p.G * D; idx += WAVES * 64)
+    for (int idx = lane; idx < p.G * D; idx += 64)
       p.o_part[((size_t)(row0 + idx / D) * p.nsplit + split_idx) * D + idx % D] = 0.f;
-    if (tid < p.G) p.lse_part[(size_t)(row0 + tid) * p.nsplit + split_idx] = kNegInf;
+    if (lane < p.G) p.lse_part[(size_t)(row0 + lane) * p.nsplit + split_idx] = kNegInf;
     return;
   }
 
-  // query fragments: B operand of S^T (columns m < G are real heads)
+  // query fragments: B operand of S^T (columns m16 < G are real heads)
   u32x4 qf[NKK];
   {
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + ((size_t)(row0 + m16) * D) * 2;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + (size_t)(row0 + m16) * ROWB;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qf[kk] = m16 < p.G ? ldg16(qrow + (32 * kk + 8 * qq) * 2) : u32x4{0, 0, 0, 0};
+      qf[kk] = m16 < p.G ? ldg16(qrow + 64 * kk + 16 * qq) : u32x4{0, 0, 0, 0};
   }
 
   const size_t kv_base = ((size_t)b * p.Hkv + kvh) * p.cap;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.kc) + kv_base * D * 2;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.vc) + kv_base * D * 2;
-  uint16_t* vtw = vt[wave];
-  const int vdc = lane & 15, vtg = lane >> 4;  // V staging: d chunk, token group of 8
-  const int vpos = 16 * (vtg & 1) + 4 * (vtg >> 1);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.kc) + kv_base * ROWB;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.vc) + kv_base * ROWB;
+  // V staging: lane holds chunk vdc of rows 8 vtg .. 8 vtg + 7
+  const int vdc = lane & 15, vtg = lane >> 4;
+  // transposed V reads: group qq reads rows 4 qq + (rr >> 2) (+ 16), dims 16 db + 4 (rr & 3)
+  const int rr = lane & 15;
+  int voff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int row = 4 * qq + (rr >> 2), d = 16 * db + 4 * (rr & 3);
+    voff[db] = row * ROWB + 16 * ((d >> 3) ^ (2 * (row & 7))) + 2 * (d & 7);
+  }
+
+  // rows past the split re-read the split's last row: their scores are masked
+  // and their probabilities are exactly zero
+  auto load = [&](u32x4 (&kf)[2][NKK], u32x4 (&vr)[8], int c0) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int tok = min(c0 + 16 * tb + m16, s1 - 1);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kf[tb][kk] = ldg16_stream(kbase + (size_t)tok * ROWB + 64 * kk + 16 * qq);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int tok = min(c0 + 8 * vtg + r, s1 - 1);
+      vr[r] = ldg16_stream(vbase + (size_t)tok * ROWB + 16 * vdc);
+    }
+  };
 
   f32x4 acc_o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int c0 = s0 + 32 * wave; c0 < s1; c0 += 32 * WAVES) {
-    u32x4 kf[2][NKK];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int tok = c0 + 16 * tb + m16;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        kf[tb][kk] = tok < s1 ? ldg16(kbase + ((size_t)tok * D + 32 * kk + 8 * qq) * 2) : u32x4{0, 0, 0, 0};
-    }
-    u32x4 vr[8];
+  auto process = [&](const u32x4 (&kf)[2][NKK], const u32x4 (&vr)[8], int c0) {
+    // V rows of the chunk -> LDS (row-major, swizzled)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int tok = c0 + 8 * vtg + r;
-      vr[r] = tok < s1 ? ldg16(vbase + ((size_t)tok * D + 8 * vdc) * 2) : u32x4{0, 0, 0, 0};
+      const int row = 8 * vtg + r;
+      *reinterpret_cast<u32x4*>(vs + row * ROWB + 16 * (vdc ^ (2 * (row & 7)))) = vr[r];
     }
-
-    // S^T = K Q^T: lane holds slots 16 tb + 4 qq + i for query column m16
+    // S^T = K Q^T: lane holds slots 16 tb + 4 qq + i of query column m16
     f32x4 sacc[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -109,24 +128,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_split_kernel(const Deco
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) sacc[tb] = Tag::mfma16(kf[tb][kk], qf[kk], sacc[tb]);
     }
-
-    // V^T for this chunk -> this wave's LDS area
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = i >> 1;
-      uint16_t* dst = vtw + (8 * vdc + i) * VP + vpos;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 a0 = vr[4 * h], a1 = vr[4 * h + 1], a2 = vr[4 * h + 2], a3 = vr[4 * h + 3];
-        u32x2 o;
-        o[0] = (i & 1) ? ((a0[e] >> 16) | (a1[e] & 0xffff0000u)) : ((a0[e] & 0xffffu) | (a1[e] << 16));
-        o[1] = (i & 1) ? ((a2[e] >> 16) | (a3[e] & 0xffff0000u)) : ((a2[e] & 0xffffu) | (a3[e] << 16));
-        *reinterpret_cast<u32x2*>(dst + 8 * h) = o;
-      }
-    }
-
-    // online softmax over the chunk's 32 slots
-    float s[8];
+    float sv[8];
     float mx = kNegInf;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_split_kernel(const Deco
       for (int i = 0; i < 4; ++i) {
         const int tok = c0 + 16 * tb + 4 * qq + i;
         const float x = tok < s1 ? sacc[tb][i] * p.scale_log2 : kNegInf;
-        s[4 * tb + i] = x;
+        sv[4 * tb + i] = x;
         mx = fmaxf(mx, x);
       }
     mx = wave_max_xor(mx, 16);
@@ -142,61 +144,54 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_split_kernel(const Deco
     const float m_new = fmaxf(m_run, mx);  // finite: every chunk holds a valid slot
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
-    float pv[8], psum = 0.f;
+    float pv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pv[j] = fast_exp2(s[j] - m_new);
-      psum += pv[j];
-    }
-    l_run = l_run * alpha + psum;
+    for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(sv[j] - m_new);
     const u32x4 pf = {Tag::pack2(pv[0], pv[1]), Tag::pack2(pv[2], pv[3]), Tag::pack2(pv[4], pv[5]),
                       Tag::pack2(pv[6], pv[7])};
+    float ps = l_run * alpha;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ps = Tag::sum2(pf[e], ps);
+    l_run = ps;
+    // O^T += V^T P^T; slot j of quarter qq is chunk row 16 (j / 4) + 4 qq + j % 4
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
+      const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16_t, vs + voff[db]));
+      const v4i16_t x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16_t, vs + voff[db] + 16 * ROWB));
+      const u32x2 a1 = __builtin_bit_cast(u32x2, x1), a2 = __builtin_bit_cast(u32x2, x2);
       acc_o[db] *= alpha;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(vtw + (16 * db + m16) * VP + 8 * qq);
-      acc_o[db] = Tag::mfma16(a, pf, acc_o[db]);
+      acc_o[db] = Tag::mfma16(u32x4{a1[0], a1[1], a2[0], a2[1]}, pf, acc_o[db]);
     }
+  };
+
+  u32x4 kA[2][NKK], vA[8], kB[2][NKK], vB[8];
+  load(kA, vA, s0);
+#pragma unroll 1
+  for (int c0 = s0; c0 < s1; c0 += 64) {
+    const bool hasB = c0 + 32 < s1;
+    if (hasB) load(kB, vB, c0 + 32);
+    process(kA, vA, c0);
+    if (!hasB) break;
+    if (c0 + 64 < s1) load(kA, vA, c0 + 64);
+    process(kB, vB, c0 + 32);
   }
 
-  // ---- merge the waves' partials ----
+  // ---- write this split's partial: lane (m16, qq) holds O^T[16 db + 4 qq + i][m16] ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  float* ow = reinterpret_cast<float*>(vtw);  // reuse this wave's V^T area: [16][D] floats
   if (m16 < p.G) {
+    const float inv = 1.f / l_run;
+    const size_t prow = (size_t)(row0 + m16) * p.nsplit + split_idx;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ow[m16 * D + 16 * db + 4 * qq + i] = acc_o[db][i];
-    if (qq == 0) {
-      red_m[wave][m16] = m_run;
-      red_l[wave][m16] = l_run;
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < p.G * D; idx += WAVES * 64) {
-    const int mm = idx / D, d = idx % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, red_m[w][mm]);
-    float o = 0.f, l = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      const float f = fast_exp2(red_m[w][mm] - M);
-      o = fmaf(f, reinterpret_cast<const float*>(vt[w])[mm * D + d], o);
-      l = fmaf(f, red_l[w][mm], l);
-    }
-    const size_t prow = (size_t)(row0 + mm) * p.nsplit + split_idx;
-    p.o_part[prow * D + d] = o / l;
-    if (d == 0) p.lse_part[prow] = (M + __log2f(l)) * kLn2;
+      *reinterpret_cast<f32x4*>(p.o_part + prow * D + 16 * db + 4 * qq) = acc_o[db] * inv;
+    if (qq == 0) p.lse_part[prow] = (m_run + __log2f(l_run)) * kLn2;
   }
 }
 
 template <class Tag>
-static void launch_split(const DecodeGqaParams& p, int waves, dim3 grid, hipStream_t st) {
-  if (waves == 4) hipLaunchKernelGGL((decode_gqa_split_kernel<Tag, 4>), grid, dim3(256), 0, st, p);
-  else if (waves == 2) hipLaunchKernelGGL((decode_gqa_split_kernel<Tag, 2>), grid, dim3(128), 0, st, p);
-  else hipLaunchKernelGGL((decode_gqa_split_kernel<Tag, 1>), grid, dim3(64), 0, st, p);
+static void launch_split(const DecodeGqaParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((decode_gqa_split_kernel<Tag>), grid, dim3(64), 0, st, p);
 }
 
 }  // namespace attn
@@ -246,10 +241,9 @@ extern "C" attn_status attn_decode_gqa(const void* q, const void* k_cache, const
   p.lse_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + ws.lse_offset);
   p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.cap = cap; p.split = split; p.nsplit = nsplit;
   p.scale_log2 = softmax_scale * kLog2e;
-  const int waves = split >= 128 ? 4 : split / 32;
   dim3 grid(nsplit, Hkv, B);
-  if (dtype == ATTN_BF16) launch_split<Bf16Tag>(p, waves, grid, stream);
-  else launch_split<F16Tag>(p, waves, grid, stream);
+  if (dtype == ATTN_BF16) launch_split<Bf16Tag>(p, grid, stream);
+  else launch_split<F16Tag>(p, grid, stream);
   attn_status st = attn_host::launch_status();
   if (st != ATTN_OK) return st;
   launch_combine(p.o_part, p.lse_part, o, B * Hq, nsplit, D, dtype, stream);
