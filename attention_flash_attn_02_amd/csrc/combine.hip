@@ -15,9 +15,53 @@
 
 namespace attn {
 
-// One wave per row; four rows per workgroup.  Lane s holds split s's weight
-// (splits beyond 64 are folded in a loop), the weights are broadcast with
-// readlane, and the partial rows are read with independent loads.
+// One thread per (row, 4 consecutive dims): every thread recomputes the
+// row's split weights from the (cached) lse values and then reads its float4
+// of every split with independent loads.  Requires D % 4 == 0.
+__global__ __launch_bounds__(256) void combine_kernel_v4(const float* __restrict__ o_part,
+                                                         const float* __restrict__ lse_part,
+                                                         void* __restrict__ o, int R, int nsplit, int D,
+                                                         int out_dtype) {
+  const int d4n = D >> 2;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)R * d4n) return;
+  const int r = (int)(t / d4n), d = 4 * (int)(t % d4n);
+  const float* lse = lse_part + (size_t)r * nsplit;
+  float mx = kNegInf;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, lse[s]);
+  const size_t oidx = (size_t)r * D + d;
+  if (mx == kNegInf) {
+    store4(o, oidx, out_dtype, 0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const f32x4* op = reinterpret_cast<const f32x4*>(o_part + (size_t)r * nsplit * D + d);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  int s = 0;
+  for (; s + 4 <= nsplit; s += 4) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = op[(size_t)(s + u) * d4n];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = fast_exp2((lse[s + u] - mx) * kLog2e);
+      wsum += w;
+      acc += w * v[u];
+    }
+  }
+  for (; s < nsplit; ++s) {
+    const float w = fast_exp2((lse[s] - mx) * kLog2e);
+    wsum += w;
+    acc += w * op[(size_t)s * d4n];
+  }
+  const float inv = 1.f / wsum;
+  store4(o, oidx, out_dtype, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+}
+
+// General D: one wave per row, four rows per workgroup.  Lane s holds split
+// s's weight (splits beyond 64 are folded in a loop), the weights are
+// broadcast with readlane, and the partial rows are read with independent
+// loads.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       void* __restrict__ o, int R, int nsplit, int D,
@@ -66,8 +110,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
                     int out_dtype, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, o_part, lse_part, o, R,
-                     nsplit, D, out_dtype);
+  if (D % 4 == 0) {
+    const long long threads = (long long)R * (D / 4);
+    hipLaunchKernelGGL(combine_kernel_v4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       o_part, lse_part, o, R, nsplit, D, out_dtype);
+  } else {
+    hipLaunchKernelGGL(combine_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, o_part, lse_part, o, R,
+                       nsplit, D, out_dtype);
+  }
 }
 
 }  // namespace attn

@@ -32,6 +32,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Raw buffer resources (CDNA buffer descriptors): word 3 selects 32-bit
+// untyped data with no swizzle, so the range check is a plain byte-offset
+// test and an out-of-range load returns zero without a memory access.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kBufferNontemporal = 2;  // cache-policy bit: streaming (nt)
+
 // ---------------------------------------------------------------------------
 // Element types (16-bit storage types are handled as raw bit patterns)
 // ---------------------------------------------------------------------------

@@ -32,27 +32,28 @@ struct DecodeGqaParams {
 typedef __attribute__((ext_vector_type(4))) short v4i16_t;
 #define LDS_PTR(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
-// Streaming 16-byte load (non-temporal: the cache rows are read exactly once).
-__device__ inline u32x4 ldg16_stream(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
 // One wave per (split, KV head, sequence).  The split is walked in chunks of
-// 32 slots; the next chunk's K and V rows are loaded (16 B per lane, into a
-// second register set) while the current chunk is computed, so loads stay in
-// flight the whole time:
-//   * K rows are the A operand of S^T = K Q^T straight from registers;
-//   * V rows are stored row-major in this wave's LDS area (chunk swizzle
-//     2 (row & 7)) and read back transposed with ds_read_b64_tr_b16, which
-//     yields the A operand of O^T = V^T P^T directly.
+// 32 slots; the next chunks' K and V rows are loaded (into further register
+// sets) while the current chunk is computed, so loads stay in flight the
+// whole time.  Rows are loaded whole so that every L2 request is a full
+// cache line, and staged in this wave's LDS area:
+//   * K fragments (16 rows x 32 dims) are read back as the A operand of
+//     S^T = K Q^T;
+//   * V rows are read back transposed with ds_read_b64_tr_b16, which yields
+//     the A operand of O^T = V^T P^T directly.
 // The partial (normalised o, lse) of the split is written to the workspace.
-template <class Tag>
-__global__ __launch_bounds__(64) void decode_gqa_split_kernel(const DecodeGqaParams p) {
+#ifndef GQA_NBUF
+#define GQA_NBUF 2
+#endif
+
+template <class Tag, int NBUF = GQA_NBUF>
+__global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(const DecodeGqaParams p) {
   constexpr int D = 128;
   constexpr int ROWB = 2 * D;  // bytes per cache row
   constexpr int NDB = D / 16;  // 16-row blocks of O^T
   constexpr int NKK = D / 32;  // 32-wide k-steps of S^T
   __shared__ __attribute__((aligned(1024))) uint8_t vs[32 * ROWB];  // V rows of the chunk
+  __shared__ __attribute__((aligned(1024))) uint8_t ks[32 * ROWB];  // K rows of the chunk
 
   const int lane = threadIdx.x;
   const int m16 = lane & 15, qq = lane >> 4;
@@ -78,9 +79,15 @@ __global__ __launch_bounds__(64) void decode_gqa_split_kernel(const DecodeGqaPar
       qf[kk] = m16 < p.G ? ldg16(qrow + 64 * kk + 16 * qq) : u32x4{0, 0, 0, 0};
   }
 
-  const size_t kv_base = ((size_t)b * p.Hkv + kvh) * p.cap;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.kc) + kv_base * ROWB;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.vc) + kv_base * ROWB;
+  // K and V rows [s0, s1) of this (sequence, KV head) as raw buffers: a slot
+  // at or past s1 lies outside the buffer's range, so its load returns zero
+  // without touching memory and every load can be issued unconditionally
+  const size_t kv_base = ((size_t)b * p.Hkv + kvh) * p.cap + s0;
+  const int range = (s1 - s0) * ROWB;
+  const __amdgpu_buffer_rsrc_t krs_s = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.kc) + kv_base * ROWB), (short)0, range, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs_s = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.vc) + kv_base * ROWB), (short)0, range, kBufferRsrcWord3);
   // V staging: lane holds chunk vdc of rows 8 vtg .. 8 vtg + 7
   const int vdc = lane & 15, vtg = lane >> 4;
   // transposed V reads: group qq reads rows 4 qq + (rr >> 2) (+ 16), dims 16 db + 4 (rr & 3)
@@ -92,20 +99,21 @@ __global__ __launch_bounds__(64) void decode_gqa_split_kernel(const DecodeGqaPar
     voff[db] = row * ROWB + 16 * ((d >> 3) ^ (2 * (row & 7))) + 2 * (d & 7);
   }
 
-  // rows past the split re-read the split's last row: their scores are masked
-  // and their probabilities are exactly zero
-  auto load = [&](u32x4 (&kf)[2][NKK], u32x4 (&vr)[8], int c0) {
+  // K and V rows are loaded whole (a 16-lane group covers one 256-byte row),
+  // so every request to L2 is a full cache line:
+  //   K: load j, lane -> row 4 j + (lane >> 4), 16-byte chunk lane & 15
+  //   V: load r, lane -> row 8 vtg + r, chunk vdc
+  const int krow = lane >> 4, kch = lane & 15;
+  auto load = [&](u32x4 (&kr)[8], u32x4 (&vr)[8], int c0) {
+    const int cb = (c0 - s0) * ROWB;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int tok = min(c0 + 16 * tb + m16, s1 - 1);
+    for (int j = 0; j < 8; ++j)
+      kr[j] = __builtin_amdgcn_raw_buffer_load_b128(krs_s, cb + (4 * j + krow) * ROWB + 16 * kch, 0, kBufferNontemporal);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kf[tb][kk] = ldg16_stream(kbase + (size_t)tok * ROWB + 64 * kk + 16 * qq);
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int tok = min(c0 + 8 * vtg + r, s1 - 1);
-      vr[r] = ldg16_stream(vbase + (size_t)tok * ROWB + 16 * vdc);
-    }
+    for (int r = 0; r < 8; ++r)
+      vr[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs_s, cb + (8 * vtg + r) * ROWB + 16 * vdc, 0, kBufferNontemporal);
+    // keep chunks in issue order: each chunk's wait then leaves the later ones in flight
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   f32x4 acc_o[NDB];
@@ -113,20 +121,31 @@ __global__ __launch_bounds__(64) void decode_gqa_split_kernel(const DecodeGqaPar
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  auto process = [&](const u32x4 (&kf)[2][NKK], const u32x4 (&vr)[8], int c0) {
-    // V rows of the chunk -> LDS (row-major, swizzled)
+  auto process = [&](const u32x4 (&kr)[8], const u32x4 (&vr)[8], int c0) {
+    // K and V rows of the chunk -> LDS (row-major).  K chunk swizzle row & 15
+    // keeps both the row-wise stores and the 16-row fragment reads below
+    // conflict-free; V keeps 2 (row & 7) for the transposed reads.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 4 * j + krow;
+      *reinterpret_cast<u32x4*>(ks + row * ROWB + 16 * (kch ^ (row & 15))) = kr[j];
+    }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = 8 * vtg + r;
       *reinterpret_cast<u32x4*>(vs + row * ROWB + 16 * (vdc ^ (2 * (row & 7)))) = vr[r];
     }
-    // S^T = K Q^T: lane holds slots 16 tb + 4 qq + i of query column m16
+    // S^T = K Q^T: A operand = K rows 16 tb + m16, dims 32 kk + 8 qq .. + 7;
+    // lane holds slots 16 tb + 4 qq + i of query column m16
     f32x4 sacc[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) sacc[tb] = Tag::mfma16(kf[tb][kk], qf[kk], sacc[tb]);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + (16 * tb + m16) * ROWB + 16 * ((4 * kk + qq) ^ m16));
+        sacc[tb] = Tag::mfma16(a, qf[kk], sacc[tb]);
+      }
     }
     float sv[8];
     float mx = kNegInf;
@@ -164,16 +183,19 @@ __global__ __launch_bounds__(64) void decode_gqa_split_kernel(const DecodeGqaPar
     }
   };
 
-  u32x4 kA[2][NKK], vA[8], kB[2][NKK], vB[8];
-  load(kA, vA, s0);
+  // NBUF chunk buffers: while one chunk is computed, the next NBUF - 1 are in
+  // flight.  Loads are unconditional so the compiler's wait counts stay exact.
+  u32x4 kr[NBUF][8], vr[NBUF][8];
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) load(kr[i], vr[i], s0 + 32 * i);
 #pragma unroll 1
-  for (int c0 = s0; c0 < s1; c0 += 64) {
-    const bool hasB = c0 + 32 < s1;
-    if (hasB) load(kB, vB, c0 + 32);
-    process(kA, vA, c0);
-    if (!hasB) break;
-    if (c0 + 64 < s1) load(kA, vA, c0 + 64);
-    process(kB, vB, c0 + 32);
+  for (int c0 = s0; c0 < s1; c0 += 32 * NBUF) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      const int c = c0 + 32 * i;
+      load(kr[(i + NBUF - 1) % NBUF], vr[(i + NBUF - 1) % NBUF], c + 32 * (NBUF - 1));
+      if (c < s1) process(kr[i], vr[i], c);
+    }
   }
 
   // ---- write this split's partial: lane (m16, qq) holds O^T[16 db + 4 qq + i][m16] ----

@@ -9,13 +9,17 @@
 // so one pass over the cache serves all heads (16 heads fill the 16-wide N
 // side of a 16x16x32 MFMA).
 //
-// One workgroup (4 waves) per (split, sequence).  For each 32-slot chunk:
-//   * the 32 cache rows (32 KB) are staged once in LDS with full-row
-//     coalesced loads (prefetched into registers during the previous chunk);
-//   * every wave computes the same S^T = C Q^T (32 x 16) from LDS, so the
-//     online-softmax state is identical in all waves without any exchange;
-//   * each wave then owns 7 of the 28 16-row blocks of O^T = C_lat^T P^T and
-//     reads its A operand (cache rows transposed) from LDS.
+// One workgroup (4 waves) per (split, sequence); wave w owns dims
+// [128 w, 128 w + 128) of every cache row.  For each 32-slot chunk:
+//   * each wave streams its slice of the 32 rows into registers, whole rows
+//     per 16-lane group so that every L2 request is a full cache line (the
+//     next chunks' loads are in flight while the current one is computed);
+//   * the slice rows are staged in the wave's LDS area; each wave computes
+//     S^T over its slice from 16-row fragments; the four partial score tiles
+//     are summed through LDS (one barrier per chunk), so every wave holds the
+//     full scores and runs the identical online softmax;
+//   * each wave computes O^T = C_lat^T P^T for the latent dims of its slice,
+//     reading the A operand transposed with ds_read_b64_tr_b16.
 // Slots at or past kv_len are never loaded; a split that starts past kv_len
 // writes the empty partial (o = 0, lse = -inf).
 
@@ -34,21 +38,31 @@ struct DecodeMlaParams {
   float scale_log2;
 };
 
-template <class Tag>
-__global__ __launch_bounds__(256) void decode_mla_split_kernel(const DecodeMlaParams p) {
-  constexpr int DQ = 512, DL = 448;
-  constexpr int CP = DQ + 8;         // LDS row pitch (16-bit elements)
-  constexpr int NKK = DQ / 32;       // 32-wide k-steps of S^T
-  constexpr int DBW = DL / 16 / 4;   // 16-row O^T blocks per wave (7)
-  __shared__ __attribute__((aligned(16))) uint16_t cl[32 * CP];
+typedef __attribute__((ext_vector_type(4))) short v4i16_m;
+#define LDS_P(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#ifndef MLA_NBUF
+#define MLA_NBUF 4
+#endif
+
+template <class Tag, int NBUF = MLA_NBUF>
+__global__ __launch_bounds__(256, 2) void decode_mla_split_kernel(const DecodeMlaParams p) {
+  constexpr int DQ = 512, DL = 448;
+  constexpr int ROWB = 2 * DQ;     // bytes per cache row
+  constexpr int SLB = 256;         // bytes of one wave's 128-dim slice of a row
+  constexpr int NKK = 4;           // 32-wide k-steps over a slice
+  constexpr int NLB = 8;           // 16-row O^T blocks per slice
+  __shared__ __attribute__((aligned(1024))) uint8_t cl[4][32 * SLB];  // per-wave slice rows
+  __shared__ float sx[2][4][8][64];                                   // partial-score exchange
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int m16 = lane & 15, qq = lane >> 4;
   const int split_idx = blockIdx.x, b = blockIdx.y;
   const int L = min(max(p.kv_len[b], 0), p.cap);
   const int s0 = split_idx * p.split;
   const int s1 = min(s0 + p.split, L);
   const int row0 = b * p.H;
+  const int nlb = wave < 3 ? NLB : (DL - 3 * 128) / 16;  // latent blocks in this slice (8, 8, 8, 4)
 
   if (s0 >= s1) {  // empty split
     for (int idx = tid; idx < p.H * DL; idx += 256)
@@ -57,88 +71,124 @@ __global__ __launch_bounds__(256) void decode_mla_split_kernel(const DecodeMlaPa
     return;
   }
 
+  // query fragments of this wave's slice: B operand (column m16 = head)
   u32x4 qf[NKK];
   {
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + ((size_t)(row0 + m16) * DQ) * 2;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + (size_t)(row0 + m16) * ROWB + SLB * wave;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qf[kk] = m16 < p.H ? ldg16(qrow + (32 * kk + 8 * qq) * 2) : u32x4{0, 0, 0, 0};
+      qf[kk] = m16 < p.H ? ldg16(qrow + 64 * kk + 16 * qq) : u32x4{0, 0, 0, 0};
   }
+  // cache rows [s0, s1) of this sequence, this wave's slice, as a raw buffer:
+  // a slot at or past s1 lies outside the buffer's range, so its load returns
+  // zero without touching memory and every load can be issued unconditionally
+  const uint8_t* cbase = reinterpret_cast<const uint8_t*>(p.c) + ((size_t)b * p.cap + s0) * ROWB + SLB * wave;
+  const __amdgpu_buffer_rsrc_t crs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cbase), (short)0, (s1 - s0 - 1) * ROWB + SLB, kBufferRsrcWord3);
+  // loads are row-contiguous (a 16-lane group covers one 256-byte slice row),
+  // so every L2 request is a full cache line: load j, lane -> row 4 j + lrow,
+  // 16-byte chunk lch
+  const int lrow = lane >> 4, lch = lane & 15;
+  const int lane_off = lrow * ROWB + 16 * lch;
+  uint8_t* myl = cl[wave];
+  // LDS rows are swizzled by 16-byte chunk: chunk c of row r sits at c ^ swz(r),
+  // swz(r) = 2 (r & 7) + ((r >> 3) & 1).  Row-wise stores, 16-row fragment
+  // reads (one chunk of 16 rows) and the transposed reads (two adjacent chunks
+  // of 4 rows) all hit distinct bank groups.
+  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  const int aswz = swz(m16);
+  // transposed reads of the slice rows: group qq reads rows 4 qq + (rr >> 2) (+ 16)
+  const int rr = lane & 15;
+  const int vrow = 4 * qq + (rr >> 2);
+  const int vlane = vrow * SLB + 8 * (rr & 1);
+  const int vx = swz(vrow), vq = (rr & 3) >> 1;
 
-  const uint8_t* cbase = reinterpret_cast<const uint8_t*>(p.c) + ((size_t)b * p.cap) * DQ * 2;
-  const int srow = tid >> 6, scol = tid & 63;  // staging: rows srow + 4u, 16-B column scol
-  u32x4 cb[8];
-  auto load_chunk = [&](int c0) {
+  auto load = [&](u32x4 (&cf)[8], int c0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int tok = c0 + srow + 4 * u;
-      cb[u] = tok < s1 ? ldg16(cbase + ((size_t)tok * DQ + 8 * scol) * 2) : u32x4{0, 0, 0, 0};
-    }
+    for (int j = 0; j < 8; ++j)
+      cf[j] = __builtin_amdgcn_raw_buffer_load_b128(crs, lane_off + (c0 - s0 + 4 * j) * ROWB, 0, kBufferNontemporal);
+    // keep chunks in issue order: each chunk's wait then leaves the later ones in flight
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  f32x4 acc_o[DBW];
+  f32x4 acc_o[NLB];
 #pragma unroll
-  for (int i = 0; i < DBW; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NLB; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
+  int buf = 0;
 
-  load_chunk(s0);
-  for (int c0 = s0; c0 < s1; c0 += 32) {
-    __syncthreads();
+  auto process = [&](const u32x4 (&cf)[8], int c0) {
+    // slice rows -> this wave's LDS area (row-major, swizzled)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(cl + (srow + 4 * u) * CP + 8 * scol) = cb[u];
-    if (c0 + 32 < s1) load_chunk(c0 + 32);
-    __syncthreads();
-
+    for (int j = 0; j < 8; ++j) {
+      const int row = 4 * j + lrow;
+      *reinterpret_cast<u32x4*>(myl + row * SLB + 16 * (lch ^ swz(row))) = cf[j];
+    }
+    // partial S^T over this slice (A operand: rows 16 tb + m16, dims 32 kk + 8 qq .. + 7),
+    // exchanged and summed over the four slices
     f32x4 sacc[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* crow = cl + (16 * tb + m16) * CP + 8 * qq;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        sacc[tb] = Tag::mfma16(*reinterpret_cast<const u32x4*>(crow + 32 * kk), qf[kk], sacc[tb]);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(myl + (16 * tb + m16) * SLB + 16 * ((4 * kk + qq) ^ aswz));
+        sacc[tb] = Tag::mfma16(a, qf[kk], sacc[tb]);
+      }
     }
-
-    float s[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sx[buf][wave][r][lane] = sacc[r >> 2][r & 3];
+    __syncthreads();
+    float sv[8];
     float mx = kNegInf;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = c0 + 16 * tb + 4 * qq + i;
-        const float x = tok < s1 ? sacc[tb][i] * p.scale_log2 : kNegInf;
-        s[4 * tb + i] = x;
-        mx = fmaxf(mx, x);
-      }
+    for (int r = 0; r < 8; ++r) {
+      const float x = sx[buf][0][r][lane] + sx[buf][1][r][lane] + sx[buf][2][r][lane] + sx[buf][3][r][lane];
+      const int tok = c0 + 16 * (r >> 2) + 4 * qq + (r & 3);
+      sv[r] = tok < s1 ? x * p.scale_log2 : kNegInf;
+      mx = fmaxf(mx, sv[r]);
+    }
+    buf ^= 1;
     mx = wave_max_xor(mx, 16);
     mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx);  // finite: every chunk holds a valid slot
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
-    float pv[8], psum = 0.f;
+    float pv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pv[j] = fast_exp2(s[j] - m_new);
-      psum += pv[j];
-    }
-    l_run = l_run * alpha + psum;
+    for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(sv[j] - m_new);
     const u32x4 pf = {Tag::pack2(pv[0], pv[1]), Tag::pack2(pv[2], pv[3]), Tag::pack2(pv[4], pv[5]),
                       Tag::pack2(pv[6], pv[7])};
-
-    // O^T rows d = 16 db + ..., A operand slot j <-> chunk slot 16 (j/4) + 4 qq + j%4
+    float ps = l_run * alpha;
 #pragma unroll
-    for (int i = 0; i < DBW; ++i) {
-      const int d = 16 * (wave * DBW + i) + m16;
-      uint32_t a[4];
+    for (int e = 0; e < 4; ++e) ps = Tag::sum2(pf[e], ps);
+    l_run = ps;
+    // O^T += C_lat^T P^T over this slice's latent dims
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j0 = 2 * e, j1 = 2 * e + 1;
-        const uint32_t lo = cl[(16 * (j0 >> 2) + 4 * qq + (j0 & 3)) * CP + d];
-        const uint32_t hi = cl[(16 * (j1 >> 2) + 4 * qq + (j1 & 3)) * CP + d];
-        a[e] = lo | (hi << 16);
+    for (int lb = 0; lb < NLB; ++lb) {
+      if (lb < nlb) {
+        const int off = vlane + 16 * ((2 * lb + vq) ^ vx);
+        const v4i16_m x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_P(v4i16_m, myl + off));
+        const v4i16_m x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_P(v4i16_m, myl + off + 16 * SLB));
+        const u32x2 a1 = __builtin_bit_cast(u32x2, x1), a2 = __builtin_bit_cast(u32x2, x2);
+        acc_o[lb] *= alpha;
+        acc_o[lb] = Tag::mfma16(u32x4{a1[0], a1[1], a2[0], a2[1]}, pf, acc_o[lb]);
       }
-      acc_o[i] *= alpha;
-      acc_o[i] = Tag::mfma16(u32x4{a[0], a[1], a[2], a[3]}, pf, acc_o[i]);
+    }
+  };
+
+  // NBUF chunk buffers: while one chunk is computed, the next NBUF - 1 are in
+  // flight.  Loads are unconditional so the compiler's wait counts stay exact.
+  u32x4 cf[NBUF][8];
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) load(cf[i], s0 + 32 * i);
+#pragma unroll 1
+  for (int c0 = s0; c0 < s1; c0 += 32 * NBUF) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      const int c = c0 + 32 * i;
+      load(cf[(i + NBUF - 1) % NBUF], c + 32 * (NBUF - 1));
+      if (c < s1) process(cf[i], c);
     }
   }
 
@@ -148,10 +198,9 @@ __global__ __launch_bounds__(256) void decode_mla_split_kernel(const DecodeMlaPa
     const float inv = 1.f / l_run;
     const size_t prow = (size_t)(row0 + m16) * p.nsplit + split_idx;
 #pragma unroll
-    for (int i = 0; i < DBW; ++i) {
-      const int d = 16 * (wave * DBW + i) + 4 * qq;
-      *reinterpret_cast<f32x4*>(p.o_part + prow * DL + d) = acc_o[i] * inv;
-    }
+    for (int lb = 0; lb < NLB; ++lb)
+      if (lb < nlb)
+        *reinterpret_cast<f32x4*>(p.o_part + prow * DL + 128 * wave + 16 * lb + 4 * qq) = acc_o[lb] * inv;
     if (wave == 0 && qq == 0) p.lse_part[prow] = (m_run + __log2f(l_run)) * kLn2;
   }
 }
