@@ -220,7 +220,7 @@ static void launch_split(const DecodeGqaParams& p, dim3 grid, hipStream_t st) {
 
 using namespace attn;
 
-static const int kDefaultGqaSplit = 128;
+static const int kDefaultGqaSplit = 256;
 
 static int gqa_split(int split) { return split <= 0 ? kDefaultGqaSplit : split; }
 

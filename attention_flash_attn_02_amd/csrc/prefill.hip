@@ -568,34 +568,29 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
     auto kbuf = [&](int i) { return hbuf + (i & 1) * TILEB; };
     auto vbuf = [&](int i) { return hbuf + (2 + (i & 1)) * TILEB; };
 
-    // direct HBM -> LDS load of local tile i of K or V (rows past S re-read
-    // row S-1: those keys are masked and their probabilities are exactly 0)
-    auto dma = [&](const uint8_t* src, uint8_t* dst, const int* loff, int i, bool is_v) {
+    // direct HBM -> LDS load of local tile i of K or V.  The buffer resource
+    // starts at the tile's first row and ends at row S, so rows past S read
+    // as zero without a memory access (those keys are masked and their
+    // probabilities are exactly 0); all address arithmetic is scalar.
+    auto tile_rsrc = [&](const uint8_t* src, int i) {
       const int key0 = (HALVES * i + half) * BN;
-      if (key0 + BN <= p.S) {
-        const uint8_t* base = src + (size_t)key0 * ROWB;
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src + (size_t)key0 * ROWB), (short)0,
+                                               (p.S - key0) * ROWB, kBufferRsrcWord3);
+    };
+    auto dma = [&](const uint8_t* src, uint8_t* dst, const int* loff, int i) {
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src, i);
 #pragma unroll
-        for (int u = 0; u < IPW; ++u)
-          __builtin_amdgcn_global_load_lds(base + loff[u], LDS_AS(void, dst + RPI * (wq * IPW + u) * ROWB), 16, 0, 0);
-      } else {
-#pragma unroll
-        for (int u = 0; u < IPW; ++u) {
-          const int row = RPI * (wq * IPW + u) + lane / CH, phys = lane % CH;
-          const int swz = is_v ? vswz(row) : kswz(row);
-          const int key = min(key0 + row, p.S - 1);
-          __builtin_amdgcn_global_load_lds(src + (size_t)key * ROWB + 16 * (phys ^ swz),
-                                           LDS_AS(void, dst + RPI * (wq * IPW + u) * ROWB), 16, 0, 0);
-        }
-      }
+      for (int u = 0; u < IPW; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_AS(void, dst + RPI * (wq * IPW + u) * ROWB), 16, loff[u], 0, 0, 0);
     };
     u32x4 kreg[ROPE ? 2 * PAIRS : 1];
     auto load_k_regs = [&](int i) {
-      const int key = min((HALVES * i + half) * BN + kr, p.S - 1);
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, i);
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) {
         const int c = kj + 4 * u;
-        kreg[2 * u] = ldg16(kg + (size_t)key * ROWB + 16 * c);
-        kreg[2 * u + 1] = ldg16(kg + (size_t)key * ROWB + 16 * (c + CH / 2));
+        kreg[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(rs, kr * ROWB + 16 * c, 0, 0);
+        kreg[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, kr * ROWB + 16 * (c + CH / 2), 0, 0);
       }
     };
     // RoPE angle of (position key0 + r, frequency j) in revolutions:
@@ -649,14 +644,14 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
       rope_base_fill(0);
       rope_base_fill(1);
       if (exists(0)) {
-        dma(vg, vbuf(0), dv, 0, true);
+        dma(vg, vbuf(0), dv, 0);
         load_k_regs(0);
       }
       __syncthreads();
       if (exists(0)) rotate_store_k(0);
     } else if (exists(0)) {
-      dma(kg, kbuf(0), dk, 0, false);
-      dma(vg, vbuf(0), dv, 0, true);
+      dma(kg, kbuf(0), dk, 0);
+      dma(vg, vbuf(0), dv, 0);
     }
 
 #pragma unroll 1
@@ -665,9 +660,9 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
       __syncthreads();                     // ... and everybody's; stage (i+1)&1 is free
       const bool has_next = exists(i + 1);
       if (has_next) {
-        dma(vg, vbuf(i + 1), dv, i + 1, true);
+        dma(vg, vbuf(i + 1), dv, i + 1);
         if (ROPE) load_k_regs(i + 1);
-        else dma(kg, kbuf(i + 1), dk, i + 1, false);
+        else dma(kg, kbuf(i + 1), dk, i + 1);
       }
       if (ROPE) rope_base_fill(i + 2);
 
@@ -701,9 +696,11 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
           }
         }
         // ---- mask, lazy online softmax ----
+        // only tiles that cross the diagonal or the end of the sequence are
+        // masked; the empty asm keeps this a branch (not per-element selects)
         const int key0 = (HALVES * i + half) * BN;
-        const bool need_mask = (key0 + BN > p.S) || (CAUSAL && key0 + BN - 1 > pw0);
-        if (need_mask) {
+        if ((key0 + BN > p.S) || (CAUSAL && key0 + BN - 1 > pw0)) {
+          asm volatile("" ::: "memory");
           // key = key0 + 4 hh + off(nb, r) is visible iff key <= min(qpos, S - 1)
           const int lim = (CAUSAL ? min(qpos, p.S - 1) : p.S - 1) - key0 - 4 * hh;
 #pragma unroll

@@ -87,6 +87,131 @@ def time_graph(fn, steps_per_graph, replays, warmup=2):
     return s.elapsed_time(e) / (replays * steps_per_graph)
 
 
+LLC_BYTES = 256 << 20         # MI355X last-level (Infinity) cache
+
+
+def cache_sets(step_bytes):
+    """Number of input copies that makes a rotation stream from HBM."""
+    return max(2, -(-2 * LLC_BYTES // step_bytes) + 1)
+
+
+def decode_case(kind, B, split, scale, graph_steps=20, modes=("warm", "cold"), iters=50):
+    """Time one decode shape (split kernel + combine) in eager and hipGraph mode."""
+    import torch
+    import attention_flash_attn_02_amd as attn
+    from workloads import decode_gqa_inputs, decode_mla_inputs
+    dev = torch.device("cuda:0")
+    if kind == "gqa":
+        q, kc, vc, L = [t.to(dev) for t in decode_gqa_inputs(B, 16, 4, 128, 2056, 2048, "bf16")]
+        by = gqa_decode_bytes(B)
+        caches = [(kc, vc)]
+        ws = torch.empty(attn.decode_gqa_workspace_bytes(B, 16, 2056, 128, split), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        mk = lambda c: (lambda: attn.decode_gqa(q, c[0], c[1], L, scale, split=split, out=o, workspace=ws))  # noqa: E731
+    else:
+        q, cm, L = [t.to(dev) for t in decode_mla_inputs(B, 16, 448, 64, 2056, 2048, "bf16")]
+        by = mla_decode_bytes(B)
+        caches = [(cm,)]
+        ws = torch.empty(attn.decode_mla_workspace_bytes(B, 16, 2056, 448, split), dtype=torch.uint8, device=dev)
+        o = torch.empty((B, 16, 448), dtype=torch.bfloat16, device=dev)
+        mk = lambda c: (lambda: attn.decode_mla(q, c[0], L, scale, split=split, out=o, workspace=ws))  # noqa: E731
+    res = {"bytes": by}
+    for mode in modes:
+        if mode == "cold":
+            n = cache_sets(by)
+            while len(caches) < n:
+                caches.append(tuple(t.clone() for t in caches[0]))
+            fns = [mk(c) for c in caches]
+        else:
+            fns = [mk(caches[0])]
+        k = [0]
+
+        def step():
+            fns[k[0] % len(fns)]()
+            k[0] += 1
+        me = time_loop(step, max(iters, len(fns)), 5)
+        mg = time_graph(step, max(graph_steps, len(fns)) if mode == "cold" else graph_steps, 5)
+        res[mode] = {"eager_us": round(me * 1e3, 2), "graph_us": round(mg * 1e3, 2),
+                     "graph_GBs": round(by / (mg * 1e-3) / 1e9, 1),
+                     "graph_frac": round(by / (mg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "eager_GBs": round(by / (me * 1e-3) / 1e9, 1), "sets": len(fns)}
+    del caches, ws, o, q
+    torch.cuda.empty_cache()
+    return res
+
+
+def sweep(scale):
+    """Every tile configuration per shape; gap of the global configuration to the best one.
+
+    Prefill: attn_prefill_gqa_rope_with_config ids (global = 0).  Decode: the
+    split size (global = the library default), hipGraph mode, cold caches."""
+    import torch
+    import attention_flash_attn_02_amd as attn
+    from workloads import prefill_inputs
+    dev = torch.device("cuda:0")
+    out = {}
+    nconf = attn.prefill_num_configs()
+    shapes = [("C2_gqa_rope_bf16_S2048", (1, 32, 8, 2048, 128, "bf16", True, 10000.0, torch.bfloat16)),
+              ("mha_D64_noncausal_N4096_f16", (4, 32, 32, 4096, 64, "f16", False, 0.0, torch.float16)),
+              ("mha_D128_causal_N4096_f16", (4, 32, 32, 4096, 128, "f16", True, 0.0, torch.float16)),
+              ("mha_D128_causal_N16384_f16", (4, 32, 32, 16384, 128, "f16", True, 0.0, torch.float16)),
+              ("mha_D64_noncausal_N1024_f16", (4, 32, 32, 1024, 64, "f16", False, 0.0, torch.float16))]
+    for name, (B, Hq, Hkv, S, D, dt, causal, theta, odt) in shapes:
+        q, k, v = [t.to(dev) for t in prefill_inputs(B, Hq, Hkv, S, D, dt, seed=S)]
+        o = torch.empty(q.shape, dtype=odt, device=dev)
+        it = 20 if S <= 4096 else 4
+        times = {}
+        for c in range(nconf):
+            ms = time_loop(lambda: attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta,
+                                                        out=o, config=c), it, 2)
+            times[str(c)] = round(ms * 1e3, 2)
+        best = min(times.values())
+        out["prefill_" + name] = {"us": times, "global": "0", "best": min(times, key=times.get),
+                                  "gap_pct": round(100 * (times["0"] / best - 1), 2)}
+        del q, k, v, o
+    for kind, Bs, sc in (("gqa", (1, 8, 32, 64, 128), scale), ("mla", (1, 32, 128), 1 / math.sqrt(192))):
+        for Bd in Bs:
+            times = {}
+            for sp in (0, 64, 128, 256, 512):
+                r = decode_case(kind, Bd, sp, sc, modes=("cold",), iters=20)
+                times["default" if sp == 0 else str(sp)] = r["cold"]["graph_us"]
+            best = min(times.values())
+            out[f"decode_{kind}_B{Bd}"] = {"graph_us": times, "global": "default",
+                                           "best": min(times, key=times.get),
+                                           "gap_pct": round(100 * (times["default"] / best - 1), 2)}
+    gaps = [v["gap_pct"] for v in out.values()]
+    out["summary"] = {"max_gap_pct": max(gaps), "mean_gap_pct": round(sum(gaps) / len(gaps), 2)}
+    return out
+
+
+def prefill_traffic():
+    """HBM bytes per launch of the prefill step from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "prefill_gqa_rope_bf16_S2048.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            key, val = line[2:].split(": ", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    h = hashlib.sha256()
+    for f in PREFILL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+PREFILL_SOURCES = ("attention_flash_attn_02_amd/csrc/prefill.hip", "attention_flash_attn_02_amd/csrc/common.hpp")
+
+
 def cpu_baseline(budget_s=15.0):
     """Time the float64 oracle on KV groups of the full prefill workload until
     about `budget_s` seconds of CPU work (or the whole workload) is done."""
@@ -123,6 +248,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="prefill step only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the tile-config sweep")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -133,7 +259,7 @@ def main():
 
     import torch
     import attention_flash_attn_02_amd as attn
-    from workloads import decode_gqa_inputs, decode_mla_inputs, prefill_inputs
+    from workloads import prefill_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -180,7 +306,7 @@ def main():
                    "in_dtype": "bf16", "out_dtype": "bf16", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_mfma_kernel<bf16,128,causal,rope>",
+                     "traffic": prefill_traffic(), "kernel": "prefill_fwd_kernel<bf16,128,causal,rope,4 waves>",
                      "algorithmic_per_launch": flops},
     }
 
@@ -212,39 +338,22 @@ def main():
                     del qm, km, vm, om
         sec["mha_fwd_Z4_H32"] = mha
         log("mha:", json.dumps(mha))
-        # GQA decode, split 128
-        dec = {}
+        # decode: split + combine per step, warm (one cache set) and cold (the
+        # step rotates over enough cache copies that the working set exceeds
+        # twice the 256 MB last-level cache, so every step streams from HBM)
+        gqa = {}
         for Bd in (1, 8, 32, 64, 128):
-            qd, kc, vc, L = [t.to(dev) for t in decode_gqa_inputs(Bd, 16, 4, 128, 2056, 2048, "bf16")]
-            od = torch.empty_like(qd)
-            ws = torch.empty(attn.decode_gqa_workspace_bytes(Bd, 16, 2056, 128, 128), dtype=torch.uint8, device=dev)
-            fn = lambda: attn.decode_gqa(qd, kc, vc, L, scale, split=128, out=od, workspace=ws)  # noqa: E731
-            me = time_loop(fn, 50, 5)
-            mg = time_graph(fn, 20, 5)
-            by = gqa_decode_bytes(Bd)
-            dec[f"B{Bd}"] = {"eager_us": round(me * 1e3, 2), "graph_us": round(mg * 1e3, 2),
-                             "graph_GBs": round(by / (mg * 1e-3) / 1e9, 1),
-                             "graph_frac": round(by / (mg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                             "eager_GBs": round(by / (me * 1e-3) / 1e9, 1), "bytes": by}
-            del qd, kc, vc, L, od, ws
-        sec["decode_gqa_split128"] = dec
-        log("decode gqa:", json.dumps(dec))
+            gqa[f"B{Bd}"] = decode_case("gqa", Bd, 0, scale)
+            log(f"decode gqa B={Bd}:", json.dumps(gqa[f"B{Bd}"]))
+        sec["decode_gqa"] = gqa
         mla = {}
         for Bd in (1, 32, 128):
-            qm, cm, L = [t.to(dev) for t in decode_mla_inputs(Bd, 16, 448, 64, 2056, 2048, "bf16")]
-            om = torch.empty((Bd, 16, 448), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(attn.decode_mla_workspace_bytes(Bd, 16, 2056, 448, 0), dtype=torch.uint8, device=dev)
-            fn = lambda: attn.decode_mla(qm, cm, L, 1 / math.sqrt(192), out=om, workspace=ws)  # noqa: E731
-            me = time_loop(fn, 50, 5)
-            mg = time_graph(fn, 20, 5)
-            by = mla_decode_bytes(Bd)
-            mla[f"B{Bd}"] = {"eager_us": round(me * 1e3, 2), "graph_us": round(mg * 1e3, 2),
-                             "graph_GBs": round(by / (mg * 1e-3) / 1e9, 1),
-                             "graph_frac": round(by / (mg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                             "eager_GBs": round(by / (me * 1e-3) / 1e9, 1), "bytes": by}
-            del qm, cm, L, om, ws
+            mla[f"B{Bd}"] = decode_case("mla", Bd, 0, 1 / math.sqrt(192))
+            log(f"decode mla B={Bd}:", json.dumps(mla[f"B{Bd}"]))
         sec["decode_mla"] = mla
-        log("decode mla:", json.dumps(mla))
+        if not args.no_sweep:
+            sec["sweep"] = sweep(scale)
+            log("sweep:", json.dumps(sec["sweep"]))
         result["secondary"] = sec
 
     if not args.no_cpu and not args.quick:

@@ -130,7 +130,7 @@ attn_status attn_prefill_gqa_rope_with_config(const void* q, const void* k, cons
  *            bytes, 256-byte aligned; contents on entry are ignored.
  *
  * The context is cut into splits of `split` slots aligned at slot 0
- * (split <= 0 picks the library default, 128); each split's partial
+ * (split <= 0 picks the library default, 256); each split's partial
  * softmax is written to the workspace and merged by the combine step.
  * dtype: ATTN_BF16 or ATTN_F16.  D: 128.  Hq/Hkv <= 16.  split: a multiple
  * of 32 in [32, 1024].  Launches two kernels on `stream`.

@@ -105,7 +105,7 @@ def test_decode_gqa_workspace_size(lib):
     lse_bytes = B * Hq * ns * 4
     up = lambda x: -(-x // 256) * 256  # noqa: E731
     assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split) == up(o_bytes) + up(lse_bytes)
-    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 0) == lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 128)
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 0) == lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 256)
     assert lib.attn_decode_gqa_workspace_bytes(0, Hq, cap, D, split) == 0
 
 

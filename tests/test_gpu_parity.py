@@ -178,13 +178,14 @@ def test_prefill_deterministic(attn):
 # ----------------------------------------------------------------------------
 # GQA decode
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("B", [1, 8, 128])
-def test_decode_gqa_config(attn, B):
+@pytest.mark.parametrize("B,split", [(1, 128), (8, 128), (128, 128), (1, 0), (128, 0)])
+def test_decode_gqa_config(attn, B, split):
     """GQA decode: Hq=16, Hkv=4, D=128, context 2048 in capacity 2056, split
-    128, bf16; slots 2048..2055 hold NaN and must never be read."""
+    128 (the decode audit's) and the library default (split=0, the launch the
+    benchmark times), bf16; slots 2048..2055 hold NaN and must never be read."""
     q, kc, vc, L = decode_gqa_inputs(B, 16, 4, 128, 2056, 2048, "bf16", nan_tail=True)
     scale = 1 / math.sqrt(128)
-    o = attn.decode_gqa(*_dev(q, kc, vc, L), scale, split=128)
+    o = attn.decode_gqa(*_dev(q, kc, vc, L), scale, split=split)
     want = oracle.decode_gqa(to_f64(q), to_f64(kc), to_f64(vc), L.numpy(), scale)
     assert _maxerr(o, want) <= 2e-2
 
