@@ -68,22 +68,27 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S):
 
 
 @pytest.mark.parametrize("config", [0, 1])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (4, 2)])
 @pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
                                                   (128, False, True, "f16"), (64, True, True, "bf16")])
-def test_prefill_every_tile_config(attn, config, D, causal, rope, dtype):
-    """Every tile configuration of the sweep passes parity before it is timed."""
+def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype):
+    """Every tile configuration of the sweep passes parity before it is timed
+    (GQA groups of 4, 1 and 2 query heads: different row layouts per wave)."""
     assert attn.prefill_num_configs() == 2
-    q, k, v = prefill_inputs(2, 8, 2, 333, D, dtype, seed=config * 7 + D)
+    q, k, v = prefill_inputs(2, Hq, Hkv, 333, D, dtype, seed=config * 7 + D + Hq)
     theta = 10000.0 if rope else 0.0
-    o = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta, config=config)
-    want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta)
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
+                                   config=config, return_lse=True)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta,
+                                    return_lse=True)
     assert _maxerr(o, want) <= TOL[dtype]
+    assert _maxerr(lse, want_lse) <= TOL[dtype]
 
 
 def test_prefill_config_out_of_range(attn):
     q, k, v = _dev(*prefill_inputs(1, 2, 2, 16, 64, "bf16"))
     with pytest.raises(attn.AttnError):
-        attn.prefill_gqa_rope(q, k, v, 0.125, config=2)
+        attn.prefill_gqa_rope(q, k, v, 0.125, config=attn.prefill_num_configs())
 
 
 def test_prefill_rope_long_positions(attn):
