@@ -508,6 +508,25 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
   // RoPE staging: row kr, chunk pairs (kj + 4u, + CH/2); 16 consecutive lanes
   // take 16 rows at one chunk so the LDS writes hit 16 distinct bank groups
   const int kr = (htid & 15) + 16 * (htid >> 6), kj = (htid >> 4) & 3;
+  // frequency lane of the per-tile angle table, read from the kernel
+  // arguments once (not inside the key loop, where the load latency would
+  // hold up the filling wave every tile)
+  const float fhi_lane = ROPE && lane < HALF ? p.rope_fhi[lane] : 0.f;
+  const float flo_lane = ROPE && lane < HALF ? p.rope_flo[lane] : 0.f;
+  // cos / sin of the row-offset angles kr f_j of this thread's K pairs
+  // (kr < 64 and f_hi has 8 significant bits, so kr f_hi is exact)
+  float rcos[ROPE ? 8 * PAIRS : 1], rsin[ROPE ? 8 * PAIRS : 1];
+  if (ROPE) {
+#pragma unroll
+    for (int u = 0; u < PAIRS; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int j = 8 * (kj + 4 * u) + t;
+        const float rev = __builtin_amdgcn_fractf((float)kr * p.rope_fhi[j]) + (float)kr * p.rope_flo[j];
+        rcos[8 * u + t] = __builtin_amdgcn_cosf(rev);
+        rsin[8 * u + t] = __builtin_amdgcn_sinf(rev);
+      }
+  }
 
 #pragma unroll 1
   for (int itn = 0; itn < n_my; ++itn) {
@@ -593,13 +612,17 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
         kreg[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, kr * ROWB + 16 * (c + CH / 2), 0, 0);
       }
     };
-    // RoPE angle of (position key0 + r, frequency j) in revolutions:
-    //   [frac(key0 f_hi) + key0 f_lo] + r (f_hi + f_lo); the bracket is per tile
+    // RoPE angle of (position key0 + r, frequency j) = base angle of the tile
+    // (key0 f_j, reduced exactly as frac(key0 f_hi) + key0 f_lo revolutions)
+    // plus the row offset r f_j.  The table holds cos and sin of the base
+    // angles of a tile; cos and sin of the row offsets are per-thread
+    // constants, and the two are combined by the angle-addition formulas.
     auto rope_base_fill = [&](int i) {
       if (wq == 0 && lane < HALF) {
         const float key0 = (float)((HALVES * i + half) * BN);
-        rope_base[half][i & 1][lane] = __builtin_amdgcn_fractf(key0 * p.rope_fhi[lane]) + key0 * p.rope_flo[lane];
-        rope_base[half][i & 1][HALF + lane] = p.rope_fhi[lane] + p.rope_flo[lane];
+        const float rev = __builtin_amdgcn_fractf(key0 * fhi_lane) + key0 * flo_lane;
+        rope_base[half][i & 1][lane] = __builtin_amdgcn_cosf(rev);
+        rope_base[half][i & 1][HALF + lane] = __builtin_amdgcn_sinf(rev);
       }
     };
     auto rotate_store_k = [&](int i) {
@@ -613,9 +636,9 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
           float r1[2], r2[2];
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            const int j = 8 * c + 2 * e + s;
-            const float rev = fmaf((float)kr, rope_base[half][i & 1][HALF + j], rope_base[half][i & 1][j]);
-            const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+            const int j = 8 * c + 2 * e + s, t = 8 * u + 2 * e + s;
+            const float cb = rope_base[half][i & 1][j], sb = rope_base[half][i & 1][HALF + j];
+            const float cs = cb * rcos[t] - sb * rsin[t], sn = sb * rcos[t] + cb * rsin[t];
             const float x1 = Tag::to_f32(s ? (lo[e] >> 16) : (lo[e] & 0xffff));
             const float x2 = Tag::to_f32(s ? (hi[e] >> 16) : (hi[e] & 0xffff));
             r1[s] = x1 * cs - x2 * sn;

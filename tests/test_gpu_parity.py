@@ -258,6 +258,23 @@ def test_decode_gqa_hipgraph_replay(attn):
 # ----------------------------------------------------------------------------
 # MLA decode
 # ----------------------------------------------------------------------------
+def test_decode_workspace_reuse(attn):
+    """One workspace (contents on entry ignored) serves consecutive GQA and MLA
+    calls of different shapes and splits."""
+    ws = torch.empty(max(attn.decode_gqa_workspace_bytes(8, 16, 2056, 128, 64),
+                         attn.decode_mla_workspace_bytes(8, 16, 2056, 448, 64)), dtype=torch.uint8, device="cuda")
+    for B, split, lengths in ((8, 64, [2048, 1, 0, 700, 2056, 33, 64, 65]), (3, 128, [5, 2000, 129]),
+                              (8, 64, [64, 63, 2056, 1000, 0, 1, 512, 513])):
+        q, kc, vc, L = decode_gqa_inputs(B, 16, 4, 128, 2056, 0, "bf16", seed=B + split, lengths=lengths)
+        o = attn.decode_gqa(*_dev(q, kc, vc, L), 0.09, split=split, workspace=ws)
+        want = oracle.decode_gqa(to_f64(q), to_f64(kc), to_f64(vc), L.numpy(), 0.09)
+        assert _maxerr(o, want) <= 2e-2
+        qm, c, Lm = decode_mla_inputs(B, 16, 448, 64, 2056, 0, "bf16", seed=B + split + 1, lengths=lengths)
+        om = attn.decode_mla(*_dev(qm, c, Lm), 0.072, split=split, workspace=ws)
+        wantm = oracle.decode_mla(to_f64(qm), to_f64(c), Lm.numpy(), 0.072, 448)
+        assert _maxerr(om, wantm) <= 2e-2
+
+
 @pytest.mark.parametrize("B", [1, 32, 128])
 def test_decode_mla_config(attn, B):
     """Absorbed-MLA decode: H=16, latent 448 + rope 64, context 2048 in
