@@ -247,6 +247,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="prefill step only (for profiling runs)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only GQA and MLA decode at batch 128 with the default splits, `steps` calls "
+                         "each (for profiling runs); prints one JSON line of its own")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true", help="skip the tile-config sweep")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -272,6 +275,15 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    if args.decode_only:
+        out = {}
+        for kind, sc in (("gqa", 1 / math.sqrt(128)), ("mla", 1 / math.sqrt(192))):
+            r = decode_case(kind, 128, 0, sc, graph_steps=args.steps, modes=("cold",), iters=args.steps)
+            out[f"decode_{kind}_B128"] = r
+            log(f"decode {kind} B=128:", json.dumps(r))
+        print(json.dumps({"decode_only": out}), flush=True)
+        return
 
     # ---- the step: causal GQA prefill with fused RoPE, full workload ----
     B, Hq, Hkv, S, D = 1, 32, 8, 2048, 128
