@@ -38,6 +38,7 @@ SIGNATURES = {
     "attn_decode_mla": (_c_int, [_vp, _vp, _vp, _vp, _vp, _sz, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _c_float, _vp]),
     "attn_combine_splits": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "attn_rope_rotate": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp]),
 }
 
 

@@ -14,6 +14,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "attn.h"
@@ -147,5 +148,35 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline attn_status launch_status() {
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+// RoPE frequencies theta^(-2i/D) in revolutions per position, f = w / (2 pi),
+// split (in double) as f_hi + f_mid + f_lo with f_hi and f_mid carrying 8
+// significant bits each: pos * f_hi and pos * f_mid are then exact in fp32
+// for pos < 2^16, and pos * f_lo stays below 2^-6 revolutions, so the device
+// reduces an angle modulo one revolution as
+//   frac(frac(pos f_hi) + frac(pos f_mid) + pos f_lo)
+// with an error of a few fp32 ulps of one revolution.  fmid may be null: the
+// two-way split f_hi + (f_mid + f_lo) is then returned in fhi / flo.
+inline void rope_freq_split(float theta, int D, float* inv_freq, float* fhi, float* flo, float* fmid = nullptr) {
+  auto top8 = [](double f) {  // f rounded down to 8 significant bits
+    if (f == 0.0) return 0.0;
+    int ex = 0;
+    const double mant = frexp(f, &ex);  // f = mant * 2^ex, mant in [0.5, 1)
+    return ldexp(floor(ldexp(mant, 8)), ex - 8);
+  };
+  for (int i = 0; i < D / 2; ++i) {
+    const double w = pow((double)theta, -2.0 * i / D);
+    const double f = w / (2.0 * 3.14159265358979323846);
+    const double hi = top8(f);
+    if (inv_freq) inv_freq[i] = (float)w;
+    fhi[i] = (float)hi;
+    if (fmid) {
+      const double mid = top8(f - hi);
+      fmid[i] = (float)mid;
+      flo[i] = (float)(f - hi - mid);
+    } else {
+      flo[i] = (float)(f - hi);
+    }
+  }
 }
 }  // namespace attn_host

@@ -56,6 +56,7 @@ struct PrefillParams {
   // the angle modulo one revolution to ~1e-7 without fp64 arithmetic.
   float rope_fhi[64];
   float rope_flo[64];
+  float rope_fmid[64];  // three-way split (f_hi + f_mid + f_lo) for the fp32 kernel
   int halves;  // MFMA kernel: 1 = 4-wave workgroups, 2 = 8-wave split-key workgroups
 };
 
@@ -834,6 +835,16 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
 // ---------------------------------------------------------------------------
 // fp32 SIMT kernel: one query row per thread, 64 rows per workgroup.
 // ---------------------------------------------------------------------------
+// cos / sin of angle pos * w_i for the fp32 kernel: the angle is reduced to
+// one revolution exactly (three-part frequency split) before the radian
+// conversion, so its error does not grow with the position.
+__device__ inline void rope_sincos_exact(const PrefillParams& p, int pos, int i, float* sn, float* cs) {
+  const float fp = (float)pos;
+  const float rev = __builtin_amdgcn_fractf(__builtin_amdgcn_fractf(fp * p.rope_fhi[i]) +
+                                            __builtin_amdgcn_fractf(fp * p.rope_fmid[i]) + fp * p.rope_flo[i]);
+  sincosf(6.283185307179586f * rev, sn, cs);
+}
+
 template <int D, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) {
   constexpr int BN = 32;
@@ -853,7 +864,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
 #pragma unroll
     for (int i = 0; i < HALF; ++i) {
       float sn, cs;
-      sincosf((float)qpos * p.inv_freq[i], &sn, &cs);
+      rope_sincos_exact(p, qpos, i, &sn, &cs);
       const float x1 = q[i], x2 = q[i + HALF];
       q[i] = x1 * cs - x2 * sn;
       q[i + HALF] = x2 * cs + x1 * sn;
@@ -876,7 +887,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
       for (int e = tid; e < BN * HALF; e += 64) {
         const int r = e / HALF, i = e % HALF;
         float sn, cs;
-        sincosf((float)(k0 + r) * p.inv_freq[i], &sn, &cs);
+        rope_sincos_exact(p, k0 + r, i, &sn, &cs);
         const float x1 = ks[r][i], x2 = ks[r][i + HALF];
         ks[r][i] = x1 * cs - x2 * sn;
         ks[r][i + HALF] = x2 * cs + x1 * sn;
@@ -995,15 +1006,9 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   p.rope = rope ? 1 : 0;
   p.halves = config == 1 ? 2 : 1;
   if (rope && S > 65536) return ATTN_ERR_UNSUPPORTED;  // exact angle reduction needs pos < 2^16
-  for (int i = 0; i < D / 2; ++i) {
-    const double w = rope ? pow((double)rope_theta, -2.0 * i / D) : 0.0;
-    const double f = w / (2.0 * 3.14159265358979323846);
-    int ex = 0;
-    const double mant = frexp(f, &ex);               // f = mant * 2^ex, mant in [0.5, 1)
-    const double hi = ldexp(floor(ldexp(mant, 8)), ex - 8);  // 8 significant bits
-    p.inv_freq[i] = (float)w;
-    p.rope_fhi[i] = (float)hi;
-    p.rope_flo[i] = (float)(f - hi);
+  if (rope) {
+    if (in_dtype == ATTN_F32) attn_host::rope_freq_split(rope_theta, D, p.inv_freq, p.rope_fhi, p.rope_flo, p.rope_fmid);
+    else attn_host::rope_freq_split(rope_theta, D, p.inv_freq, p.rope_fhi, p.rope_flo);
   }
 
   if (in_dtype == ATTN_F32) {

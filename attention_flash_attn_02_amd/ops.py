@@ -66,6 +66,32 @@ def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_th
     return (out, lse) if return_lse else out
 
 
+def rope_rotate(x, rope_theta: float, out=None, stream=None):
+    """attn_rope_rotate: rotate x [B,H,S,D] by position (rotate-half RoPE,
+    positions 0..S-1).  ``out`` may be ``x`` itself (in place)."""
+    B, H, S, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    _lib.check(_lib.lib().attn_rope_rotate(_dev(x, "x"), _dev(out, "out"), B, H, S, D, _dtype_code(x),
+                                           float(rope_theta), _stream(stream)))
+    return out
+
+
+def prefill_gqa_rope_unfused(q, k, v, softmax_scale: float, causal: bool = True, rope_theta: float = 0.0,
+                             out_dtype=None, out=None, return_lse: bool = False, q_rot=None, k_rot=None,
+                             stream=None, config=None):
+    """The unfused form of prefill_gqa_rope: attn_rope_rotate on Q and on K
+    (into ``q_rot`` / ``k_rot``, allocated if not given), then the attention
+    kernel without RoPE.  Three launches instead of one."""
+    if rope_theta > 0:
+        q = rope_rotate(q, rope_theta, out=q_rot, stream=stream)
+        k = rope_rotate(k, rope_theta, out=k_rot, stream=stream)
+    return prefill_gqa_rope(q, k, v, softmax_scale, causal=causal, rope_theta=0.0, out_dtype=out_dtype, out=out,
+                            return_lse=return_lse, stream=stream, config=config)
+
+
 def decode_gqa_workspace_bytes(B, Hq, cap, D, split=0) -> int:
     return int(_lib.lib().attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split))
 

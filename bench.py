@@ -140,6 +140,51 @@ def decode_case(kind, B, split, scale, graph_steps=20, modes=("warm", "cold"), i
     return res
 
 
+def rope_factorial(graph_steps=20, iters=50):
+    """RoPE fused into the attention kernel vs RoPE as separate kernels
+    (attn_rope_rotate on Q and K, then attention without RoPE), in eager and
+    hipGraph mode, warm (one input set) and cold (inputs rotated over enough
+    copies to exceed twice the last-level cache), on the causal GQA RoPE
+    prefill workload."""
+    import torch
+    import attention_flash_attn_02_amd as attn
+    from workloads import prefill_inputs
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, S, D = 1, 32, 8, 2048, 128
+    scale = 1 / math.sqrt(D)
+    q, k, v = [t.to(dev) for t in prefill_inputs(B, Hq, Hkv, S, D, "bf16")]
+    flops = prefill_flops(B, Hq, S, D, True)
+    set_bytes = 2 * (q.numel() + k.numel() + v.numel() + q.numel())  # q, k, v in, o out
+    out = {}
+    for mode in ("warm", "cold"):
+        n = 1 if mode == "warm" else cache_sets(set_bytes)
+        sets = [(q, k, v)] + [(q.clone(), k.clone(), v.clone()) for _ in range(n - 1)]
+        outs = [torch.empty_like(q) for _ in range(n)]
+        qr = [torch.empty_like(q) for _ in range(n)]
+        kr = [torch.empty_like(k) for _ in range(n)]
+        for variant in ("fused", "unfused"):
+            if variant == "fused":
+                fns = [lambda i=i: attn.prefill_gqa_rope(*sets[i], scale, causal=True, rope_theta=10000.0, out=outs[i])
+                       for i in range(n)]
+            else:
+                fns = [lambda i=i: attn.prefill_gqa_rope_unfused(*sets[i], scale, causal=True, rope_theta=10000.0,
+                                                                 out=outs[i], q_rot=qr[i], k_rot=kr[i])
+                       for i in range(n)]
+            c = [0]
+
+            def step():
+                fns[c[0] % n]()
+                c[0] += 1
+            me = time_loop(step, max(iters, n), 5)
+            mg = time_graph(step, max(graph_steps, n), 5)
+            out[f"{variant}_{mode}"] = {"eager_us": round(me * 1e3, 2), "graph_us": round(mg * 1e3, 2),
+                                        "eager_tflops": round(flops / (me * 1e-3) / 1e12, 1),
+                                        "graph_tflops": round(flops / (mg * 1e-3) / 1e12, 1), "sets": n}
+        del sets, outs, qr, kr
+        torch.cuda.empty_cache()
+    return out
+
+
 def sweep(scale):
     """Every tile configuration per shape; gap of the global configuration to the best one.
 
@@ -363,6 +408,8 @@ def main():
             mla[f"B{Bd}"] = decode_case("mla", Bd, 0, 1 / math.sqrt(192))
             log(f"decode mla B={Bd}:", json.dumps(mla[f"B{Bd}"]))
         sec["decode_mla"] = mla
+        sec["rope_fusion_factorial"] = rope_factorial()
+        log("rope fusion:", json.dumps(sec["rope_fusion_factorial"]))
         if not args.no_sweep:
             sec["sweep"] = sweep(scale)
             log("sweep:", json.dumps(sec["sweep"]))

@@ -115,6 +115,28 @@ attn_status attn_prefill_gqa_rope_with_config(const void* q, const void* k, cons
                                               int config, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Standalone RoPE rotation (the unfused form of the prefill's RoPE step; the
+ * shape-adaptive attention lesson page, rows "What was tried" and "Actual
+ * result", compares RoPE fused into attention with separate RoPE kernels).
+ *
+ *   x, y  [B, H, S, D]  dtype; y may equal x (in place), otherwise the two
+ *         must not overlap.
+ *
+ * Row (b, h, s) is rotated as in attn_prefill_gqa_rope: the rotate-half pair
+ * (i, i + D/2) turns by angle s * rope_theta^(-2i/D), positions 0..S-1,
+ * computed in fp32 and rounded once to dtype.  Applying it to Q and K and
+ * then calling attn_prefill_gqa_rope with rope_theta <= 0 gives the same
+ * attention as the fused call (up to rounding order).
+ *
+ * dtype: ATTN_F32, ATTN_F16 or ATTN_BF16 (ATTN_FP8_E5M2: ATTN_ERR_UNSUPPORTED).
+ * D even, at most 256, half rows a whole number of 16-byte chunks (D % 16 == 0
+ * for 16-bit types, D % 8 == 0 for fp32); S <= 65536; rope_theta a positive
+ * finite number (ATTN_ERR_SHAPE otherwise).  Launches one kernel on `stream`.
+ * ------------------------------------------------------------------------ */
+attn_status attn_rope_rotate(const void* x, void* y, int B, int H, int S, int D, attn_dtype dtype,
+                             float rope_theta, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Split-context GQA decode ("flash-decoding"): one new query token per
  * sequence against a static KV cache.
  *

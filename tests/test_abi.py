@@ -139,6 +139,18 @@ def test_combine_rejects(lib):
     assert f(P + 1, P, P2, 4, 3, 128, _lib.ATTN_F32, None) == 4
 
 
+def test_rope_rejects(lib):
+    def rope(x=P, y=P, B=1, H=2, S=16, D=128, dt=_lib.ATTN_BF16, theta=10000.0):
+        return lib.attn_rope_rotate(x, y, B, H, S, D, dt, theta, None)
+    assert rope(x=None) == 1
+    assert rope(S=0) == 2 and rope(D=63) == 2
+    assert rope(theta=0.0) == 2 and rope(theta=float("nan")) == 2 and rope(theta=float("inf")) == 2
+    assert rope(dt=_lib.ATTN_FP8_E5M2) == 6 and rope(dt=9) == 3
+    assert rope(D=258) == 6 and rope(D=24) == 6       # half rows not whole 16-byte chunks (16-bit)
+    assert rope(S=65537) == 6
+    assert rope(x=P + 8) == 4
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

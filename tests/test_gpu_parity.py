@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import (decode_gqa_inputs, decode_mla_inputs, prefill_inputs, split_partials,
+from workloads import (decode_gqa_inputs, decode_mla_inputs, prefill_inputs, randn, split_partials,
                        to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -43,6 +43,22 @@ def _maxerr(gpu, want):
 # ----------------------------------------------------------------------------
 # Prefill
 # ----------------------------------------------------------------------------
+@pytest.mark.parametrize("S,rows", [(300, None), (4096, [0, 1, 2047, 4000, 4095])])
+def test_prefill_f32_rope(attn, S, rows):
+    """fp32 prefill with RoPE (the SIMT kernel): every element at S=300,
+    sampled rows up to position 4095, at the fp32 tolerance."""
+    q, k, v = prefill_inputs(1, 4, 2, S, 64, "f32", seed=S)
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.125, causal=True, rope_theta=10000.0)
+    if rows is None:
+        want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 0.125, True, 10000.0)
+        assert _maxerr(o, want) <= TOL["f32"]
+    else:
+        qd, kd, vd = to_f64(q), to_f64(k), to_f64(v)
+        for h in (0, 3):
+            want = oracle.prefill_rows(qd, kd, vd, 0.125, True, 10000.0, 0, h, rows)[0]
+            assert _maxerr(o[0, h, rows], want) <= TOL["f32"]
+
+
 def test_tiny_f32_full(attn):
     """Tiny causal GQA prefill, fp32: B=1, Hq=4, Hkv=2, S=128, D=64, scale 1/8."""
     q, k, v = prefill_inputs(1, 4, 2, 128, 64, "f32")
@@ -178,6 +194,42 @@ def test_prefill_deterministic(attn):
     a = attn.prefill_gqa_rope(q, k, v, 0.09, causal=True, rope_theta=10000.0)
     b = attn.prefill_gqa_rope(q, k, v, 0.09, causal=True, rope_theta=10000.0)
     assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# Standalone RoPE (the unfused form) and the unfused prefill
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,D,S", [("bf16", 128, 333), ("f16", 64, 2048), ("f32", 128, 77), ("f32", 64, 16384)])
+def test_rope_rotate_matches_oracle(attn, dtype, D, S):
+    """attn_rope_rotate against the oracle's explicit rotation; fp32 at
+    position 16383 checks the exact angle reduction."""
+    x = randn((2, 3, S, D), dtype, seed=S + D, name="rope_x")
+    want = oracle.rope_rotate(to_f64(x), np.arange(S), 10000.0)
+    got = attn.rope_rotate(x.cuda(), 10000.0)
+    assert _maxerr(got, want) <= TOL[dtype]
+
+
+def test_rope_rotate_in_place(attn):
+    x = randn((1, 4, 100, 128), "bf16", seed=3, name="rope_x")
+    want = attn.rope_rotate(x.cuda(), 500000.0).cpu()
+    xd = x.cuda()
+    attn.rope_rotate(xd, 500000.0, out=xd)
+    assert torch.equal(xd.cpu(), want)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,S", [(128, 32, 8, 2048), (64, 4, 4, 333)])
+def test_prefill_unfused_matches_oracle(attn, D, Hq, Hkv, S):
+    """RoPE on Q and K by attn_rope_rotate, then attention without RoPE: the
+    same result as the fused call (sampled rows at the full C2 shape)."""
+    q, k, v = prefill_inputs(1, Hq, Hkv, S, D, "bf16", seed=S)
+    o = attn.prefill_gqa_rope_unfused(*_dev(q, k, v), 1 / math.sqrt(D), causal=True, rope_theta=10000.0)
+    rows = [0, 1, S // 2, S - 1]
+    qd, kd, vd = to_f64(q), to_f64(k), to_f64(v)
+    for h in (0, Hq - 1):
+        want = oracle.prefill_rows(qd, kd, vd, 1 / math.sqrt(D), True, 10000.0, 0, h, rows)[0]
+        assert _maxerr(o[0, h, rows], want) <= TOL["bf16"]
+    fused = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=True, rope_theta=10000.0)
+    assert _maxerr(o, to_f64(fused)) <= TOL["bf16"]
 
 
 # ----------------------------------------------------------------------------

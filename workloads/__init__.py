@@ -32,7 +32,7 @@ SEED = 123
 # Per-tensor seed offsets: each named tensor of a workload draws from its own
 # stream so that changing one shape does not shift the others.
 _OFFSETS = {"q": 0, "k": 1, "v": 2, "kv": 3, "q_nope": 4, "q_rope": 5,
-            "w_uk": 6, "w_uv": 7, "c": 8, "part_o": 9, "part_lse": 10}
+            "w_uk": 6, "w_uv": 7, "c": 8, "part_o": 9, "part_lse": 10, "rope_x": 11}
 
 CONFIGS = {
     "tiny_f32": dict(B=1, Hq=4, Hkv=2, S=128, D=64, dtype="f32", out="f32",
