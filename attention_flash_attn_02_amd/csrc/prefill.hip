@@ -833,6 +833,445 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
 }
 
 // ---------------------------------------------------------------------------
+// Software-pipelined MFMA kernel.  Same work split and LDS layout as
+// prefill_fwd_kernel with 4-wave workgroups (32 query rows per wave, 64-key
+// tiles), but the key loop is skewed by one tile: while a wave exponentiates
+// the scores of tile i it already issues the S = K Q^T MFMAs of tile i+1, so
+// the matrix cores stay busy through the softmax instead of waiting for it.
+// K is therefore staged one tile ahead of V.  With RoPE the raw K tile is
+// DMA'd to LDS and rotated in place by the wave that loaded its rows.  The
+// row max of tile i+1 is taken while the PV MFMAs of tile i run, and the V
+// loads of tile i+1 are issued between the two phases instead of in one
+// burst after the barrier.  On gfx950 this measures about equal to the
+// unskewed kernel (ahead only at long sequences): it is a sweep
+// configuration, not the default.
+// ---------------------------------------------------------------------------
+template <class Tag, int D, bool CAUSAL, bool ROPE>
+__global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParams p) {
+  constexpr int BN = 64;
+  constexpr int ROWB = D * 2;        // bytes per K/V row
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int TILEB = BN * ROWB;   // bytes of one K or V tile
+  constexpr int RPI = 64 / CH;       // rows per wave-wide direct load
+  constexpr int IPW = BN / RPI / 4;  // direct loads per wave per tile
+  constexpr int NKK = D / 16, NDB = D / 32, HALF = D / 2, PAIRS = D / 64;
+  constexpr float kLazy = 8.f;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];  // [K0 K1 V0 V1]
+  __shared__ float rope_base[2][ROPE ? D : 1];                        // [slot][cos | sin]
+
+  // chunk swizzles (see prefill_fwd_kernel)
+  auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+  auto vswz = [](int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int m = lane & 31, hh = lane >> 5;
+  const int g = lane >> 4, rr = lane & 15;
+
+  int koff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = m * ROWB + 16 * ((2 * kk + hh) ^ kswz(m));
+  int voff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d = 32 * db + 16 * (g & 1) + 4 * (rr & 3);
+    const int key = 4 * (g >> 1) + (rr >> 2);
+    voff[db] = key * ROWB + 16 * ((d >> 3) ^ vswz(key)) + 2 * (d & 7);
+  }
+  // direct-load lane offsets for the first of the wave's IPW loads; wave wq
+  // loads rows 16 wq .. 16 wq + 15 of a tile, RPI rows per load.  Load u
+  // reads RPI u rows further on and, since the V swizzle does not depend on
+  // the row bits that u sets, V load u is load 0 moved by u RPI ROWB bytes
+  // (an instruction offset, applied to both the global and the LDS
+  // address).  The K swizzle XORs 4 u into the chunk index of those rows,
+  // so K load u also XORs 64 u into the byte offset (no carry: the row part
+  // of the offset is a multiple of 128 and the chunk part stays below it).
+  const int row0 = RPI * wq * IPW + lane / CH, phys0 = lane % CH;
+  const int dk0 = row0 * ROWB + 16 * (phys0 ^ kswz(row0));
+  const int dv0 = row0 * ROWB + 16 * (phys0 ^ vswz(row0));
+
+  // causal: the second half of the grid takes the short items in reverse
+  // order so that workgroups k and k + n/2 carry complementary work
+  const int per_ptile = p.B * p.Hkv * p.n_hgroups;
+  const int n_items = p.n_ptiles * per_ptile;
+  const int half_items = (n_items + 1) / 2;
+  const int item = (CAUSAL && (int)blockIdx.x >= half_items) ? n_items - 1 - ((int)blockIdx.x - half_items)
+                                                             : (int)blockIdx.x;
+  // RoPE on K: this thread rotates row kr (one of the rows its own wave
+  // loaded) at chunk pairs (kj + 4u, + CH/2)
+  const int kr = (lane & 15) + 16 * wq, kj = lane >> 4;
+  const float fhi_lane = ROPE && lane < HALF ? p.rope_fhi[lane] : 0.f;
+  const float flo_lane = ROPE && lane < HALF ? p.rope_flo[lane] : 0.f;
+  float rcos[ROPE ? 8 * PAIRS : 1], rsin[ROPE ? 8 * PAIRS : 1];
+  if (ROPE) {
+#pragma unroll
+    for (int u = 0; u < PAIRS; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int j = 8 * (kj + 4 * u) + t;
+        const float rev = __builtin_amdgcn_fractf((float)(kr & 63) * p.rope_fhi[j]) + (float)(kr & 63) * p.rope_flo[j];
+        rcos[8 * u + t] = __builtin_amdgcn_cosf(rev);
+        rsin[8 * u + t] = __builtin_amdgcn_sinf(rev);
+      }
+  }
+
+  const int ptile = p.n_ptiles - 1 - item / per_ptile;
+  int rest = item % per_ptile;
+  const int hg = rest % p.n_hgroups;
+  rest /= p.n_hgroups;
+  const int kvh = rest % p.Hkv;
+  const int b = rest / p.Hkv;
+  const int head = kvh * p.G + hg * p.GP + (wq % p.GP);
+  const int p0 = ptile * p.P;
+  const int pw0 = p0 + (wq / p.GP) * 32;
+  const int kend = CAUSAL ? min(p.S, p0 + p.P) : p.S;
+  const int n = (kend + BN - 1) / BN;
+  const int qpos = pw0 + m;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), rotated in registers ----
+  uint32_t qf[D / 4];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head) * p.S + qpos) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 w = qpos < p.S ? ldg16(qrow + 16 * kk + 8 * hh) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
+    }
+    if (ROPE) {
+#pragma unroll
+      for (int kk = 0; kk < NKK / 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w1 = qf[4 * kk + e], w2 = qf[4 * (kk + NKK / 2) + e];
+          float r1[2], r2[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int fi = 16 * kk + 8 * hh + 2 * e + s;
+            const float rev = __builtin_amdgcn_fractf((float)qpos * p.rope_fhi[fi]) + (float)qpos * p.rope_flo[fi];
+            const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+            const float x1 = Tag::to_f32(s ? (w1 >> 16) : (w1 & 0xffff));
+            const float x2 = Tag::to_f32(s ? (w2 >> 16) : (w2 & 0xffff));
+            r1[s] = x1 * cs - x2 * sn;
+            r2[s] = x2 * cs + x1 * sn;
+          }
+          qf[4 * kk + e] = Tag::pack2(r1[0], r1[1]);
+          qf[4 * (kk + NKK / 2) + e] = Tag::pack2(r2[0], r2[1]);
+        }
+    }
+  }
+
+  const size_t kv_row0 = ((size_t)b * p.Hkv + kvh) * p.S;
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k) + kv_row0 * ROWB;
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.v) + kv_row0 * ROWB;
+  auto exists = [&](int i) { return i < n; };
+  auto kbuf = [&](int i) { return smem + (i & 1) * TILEB; };
+  auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * TILEB; };
+
+  // direct HBM -> LDS load of tile i of K or V; rows past S read as zero
+  auto dma = [&](const uint8_t* src, uint8_t* dst, bool is_k, int i) {
+    const int key0 = i * BN;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(src + (size_t)key0 * ROWB), (short)0, (p.S - key0) * ROWB, kBufferRsrcWord3);
+    auto* ld = LDS_AS(void, dst + RPI * wq * IPW * ROWB);
+    // (the instruction offset must be a constant: loads written out)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ld, 16, is_k ? dk0 : dv0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ld, 16, is_k ? (dk0 ^ 64) : dv0, 0, RPI * ROWB, 0);
+    if constexpr (IPW == 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ld, 16, is_k ? (dk0 ^ 128) : dv0, 0, 2 * RPI * ROWB, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ld, 16, is_k ? (dk0 ^ 192) : dv0, 0, 3 * RPI * ROWB, 0);
+    }
+  };
+  // cos / sin of the base angle key0 f_j of tile i into table slot i & 1
+  auto rope_base_fill = [&](int i) {
+    if (wq == 0 && lane < HALF) {
+      const float key0 = (float)(i * BN);
+      const float rev = __builtin_amdgcn_fractf(key0 * fhi_lane) + key0 * flo_lane;
+      rope_base[i & 1][lane] = __builtin_amdgcn_cosf(rev);
+      rope_base[i & 1][HALF + lane] = __builtin_amdgcn_sinf(rev);
+    }
+  };
+  // rotate this thread's pairs of K tile i in place (angle addition of the
+  // tile base angle and the row offset angle)
+  auto rotate_k = [&](int i) {
+    uint8_t* kb = kbuf(i);
+#pragma unroll
+    for (int u = 0; u < PAIRS; ++u) {
+      const int c = kj + 4 * u;
+      u32x4* plo = reinterpret_cast<u32x4*>(kb + kr * ROWB + 16 * (c ^ kswz(kr)));
+      u32x4* phi = reinterpret_cast<u32x4*>(kb + kr * ROWB + 16 * ((c + CH / 2) ^ kswz(kr)));
+      u32x4 lo = *plo, hi = *phi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float r1[2], r2[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int j = 8 * c + 2 * e + s, t = 8 * u + 2 * e + s;
+          const float cb = rope_base[i & 1][j], sb = rope_base[i & 1][HALF + j];
+          const float cs = cb * rcos[t] - sb * rsin[t], sn = sb * rcos[t] + cb * rsin[t];
+          const float x1 = Tag::to_f32(s ? (lo[e] >> 16) : (lo[e] & 0xffff));
+          const float x2 = Tag::to_f32(s ? (hi[e] >> 16) : (hi[e] & 0xffff));
+          r1[s] = x1 * cs - x2 * sn;
+          r2[s] = x2 * cs + x1 * sn;
+        }
+        lo[e] = Tag::pack2(r1[0], r1[1]);
+        hi[e] = Tag::pack2(r2[0], r2[1]);
+      }
+      *plo = lo;
+      *phi = hi;
+    }
+  };
+
+  // ---- running state ----
+  f32x16 acc_o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
+  float m_ref = kNegInf;  // exponent reference (scaled log2 domain), equal in both lanes of a row
+  float l_run = 0.f;      // sum over this lane's keys of exp2(s - m_ref)
+
+  // S^T of tile i into acc (MFMA j: k-step j / 2, key block j % 2); K
+  // fragments read from LDS three MFMAs ahead
+  auto k_frag = [&](const uint8_t* kb, int j) {
+    return *reinterpret_cast<const u32x4*>(kb + koff[j >> 1] + 32 * (j & 1) * ROWB);
+  };
+  auto scores = [&](int i, f32x16 (&acc)[2]) {
+    const uint8_t* kb = kbuf(i);
+    constexpr int NJ = 2 * NKK;
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+    u32x4 fa[4];
+    fa[0] = k_frag(kb, 0);
+    fa[1] = k_frag(kb, 1);
+    fa[2] = k_frag(kb, 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 3 < NJ) fa[(j + 3) % 4] = k_frag(kb, j + 3);
+      const int kk = j >> 1;
+      const u32x4 bq = {qf[4 * kk], qf[4 * kk + 1], qf[4 * kk + 2], qf[4 * kk + 3]};
+      acc[j & 1] = Tag::mfma32(fa[j % 4], bq, acc[j & 1]);
+    }
+  };
+  // probabilities of the scores in acc (bf16/f16, B-operand layout of PV)
+  // and their row sum
+  // (MASK: keys past lim get probability 0)
+  auto exponentiate = [&](f32x16 (&acc)[2], float m_use, uint32_t (&pf)[4][4], int lim, auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
+    auto arg = [&](int nb, int r) {
+      const float x = fmaf(acc[nb][r], p.scale_log2, -m_use);
+      return (MASK && 32 * nb + 8 * (r >> 2) + (r & 3) > lim) ? kNegInf : x;
+    };
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = fast_exp2(arg(nb, r));
+        const float e1 = fast_exp2(arg(nb, r + 1));
+        const uint32_t pk = Tag::pack2(e0, e1);
+        pf[2 * nb + (r >> 3)][(r & 7) >> 1] = pk;
+        l_run = Tag::sum2(pk, l_run);
+      }
+  };
+  // mask, row max and (lazy) rescale for the scores of tile i; returns the
+  // exponent offset for exponentiate
+  // scaled row max of the scores in acc (both lanes of a row agree); a
+  // tree of depth 4 rather than a 16-deep chain
+  auto row_max = [&](const f32x16 (&acc)[2], int lim, auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
+    auto val = [&](int e) {  // element e = 16 nb + r
+      const int nb = e >> 4, r = e & 15;
+      return (MASK && 32 * nb + 8 * (r >> 2) + (r & 3) > lim) ? kNegInf : acc[nb][r];
+    };
+    float t1[11];
+#pragma unroll
+    for (int u = 0; u < 10; ++u) t1[u] = fmaxf(fmaxf(val(3 * u), val(3 * u + 1)), val(3 * u + 2));
+    t1[10] = fmaxf(val(30), val(31));
+    const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+    const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(t1[9], t1[10]);
+    return pair_max32(fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d))) * p.scale_log2;
+  };
+  // tiles that cross the diagonal or the end of the sequence are masked:
+  // key offset o inside the tile (this lane's keys start at 4 hh) is
+  // visible iff o <= lim
+  auto needs_mask = [&](int i) { return (i * BN + BN > p.S) || (CAUSAL && i * BN + BN - 1 > pw0); };
+  auto mask_lim = [&](int i) { return (CAUSAL ? min(qpos, p.S - 1) : p.S - 1) - i * BN - 4 * hh; };
+  // (lazy) rescale for the scores of tile i with row max mx (the unmasked
+  // max taken while the previous tile's PV ran, or the masked max); returns
+  // the exponent offset for exponentiate
+  auto softmax_head = [&](float mx) {
+    if (__ballot(mx > m_ref + kLazy)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = fast_exp2(m_ref - m_new);  // 0 when m_ref = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      m_ref = m_new;
+    }
+    return m_ref == kNegInf ? 0.f : m_ref;
+  };
+  // O^T += V^T P^T for tile i; transposing reads issued two MFMAs ahead
+  auto pv = [&](int i, const uint32_t (&pf)[4][4], auto own_schedule) {
+    const uint8_t* vb = vbuf(i);
+    constexpr int NJ = NDB * 4;  // MFMA j = NDB c + db (consecutive MFMAs use different accumulators)
+    auto rd = [&](int j) {
+      const int db = j % NDB, c = j / NDB;
+      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16, vb + voff[db] + 16 * c * ROWB));
+      const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16, vb + voff[db] + (16 * c + 8) * ROWB));
+      const u32x2 a1 = __builtin_bit_cast(u32x2, x1), a2 = __builtin_bit_cast(u32x2, x2);
+      return u32x4{a1[0], a1[1], a2[0], a2[1]};
+    };
+    u32x4 fa[3];
+    fa[0] = rd(0);
+    fa[1] = rd(1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 2 < NJ) fa[(j + 2) % 3] = rd(j + 2);
+      const int c = j / NDB;
+      const u32x4 bp = {pf[c][0], pf[c][1], pf[c][2], pf[c][3]};
+      acc_o[j % NDB] = Tag::mfma32(fa[j % 3], bp, acc_o[j % NDB]);
+    }
+    if constexpr (decltype(own_schedule)::value) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+  };
+
+  // One key tile that has a successor: cur holds S of tile i, nxt receives
+  // S of tile i + 1.
+  //   top:  tile i's V and tile i+1's K have landed (and K is rotated);
+  //         issue V(i+1) and K(i+2) into the stages of tiles i-1 and i
+  //   body: softmax of tile i with the MFMAs of S(i+1) interleaved, then PV.
+  // A wave whose rows end inside tile i still computes S(i+1) (unused): that
+  // keeps the interleaved region one basic block.
+  float mx_pre = kNegInf;  // unmasked scaled row max of the next tile's scores
+  // the item's last tile, masked (done without a successor to overlap with)
+  auto tail_block = [&](int i, f32x16 (&cur)[2]) {
+    const int lim = mask_lim(i);
+    uint32_t pf[4][4];
+    const float m_use = softmax_head(row_max(cur, lim, std::true_type{}));
+    exponentiate(cur, m_use, pf, lim, std::true_type{});
+    pv(i, pf, std::true_type{});
+  };
+  // One key tile with a successor: cur holds S of tile i, nxt receives S of
+  // tile i + 1.
+  //   top:  tile i's V and tile i+1's K have landed (and K is rotated);
+  //         issue K(i+2) into the stage tile i used
+  //   body: softmax of tile i with the MFMAs of S(i+1) interleaved, then PV
+  //         with the loads of V(i+1) and the row max of S(i+1) in between.
+  // LAST_TWO: tile i is the item's second to last (no K(i+2) to stage).
+  // Every wave does every tile of the item.  Tiles before the last two are
+  // never masked.  A wave's diagonal tile is n-1, or n-2 when the four
+  // waves hold consecutive 32-row blocks of one head (then the wave's last
+  // tile is fully masked, which leaves its running max, sum and output
+  // unchanged); the ragged end of the sequence falls in tile n-1.  So the
+  // last two tiles are masked and the others are not.
+  auto step = [&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto last_two) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // this thread's loads have landed
+    __syncthreads();                     // ... and everybody's; stages of tiles i-1 / i are free
+    if (!decltype(last_two)::value) dma(kg, kbuf(i + 2), true, i + 2);
+    if (ROPE) rope_base_fill(i + 3);
+    {
+      const int lim = mask_lim(i);
+      const float m_use = softmax_head(decltype(last_two)::value ? row_max(cur, lim, last_two) : mx_pre);
+      uint32_t pf[4][4];
+      scores(i + 1, nxt);
+      exponentiate(cur, m_use, pf, lim, last_two);
+      dma(vg, vbuf(i + 1), false, i + 1);
+      pv(i, pf, std::false_type{});
+      mx_pre = row_max(nxt, 0, std::false_type{});
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
+#pragma unroll
+      for (int j = 0; j < 2 * NKK; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 4 * NDB; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        if (j < IPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x402, 2, 1);
+      }
+    }
+    if (ROPE && !decltype(last_two)::value) {
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // raw K(i+2) rows of this wave have landed
+      rotate_k(i + 2);
+    }
+  };
+  // the item's last tile
+  auto last_step = [&](int i, f32x16 (&cur)[2]) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);
+    __syncthreads();
+    tail_block(i, cur);
+  };
+
+  // ---- prologue: K(0), V(0), K(1) staged (and rotated), S(0) computed ----
+  f32x16 s_a[2], s_b[2];
+  if (ROPE) {
+    rope_base_fill(0);
+    rope_base_fill(1);
+  }
+  dma(kg, kbuf(0), true, 0);
+  dma(vg, vbuf(0), false, 0);
+  if (exists(1)) dma(kg, kbuf(1), true, 1);
+  __builtin_amdgcn_s_waitcnt(0x3f70);
+  if (ROPE) {
+    __syncthreads();  // base table visible
+    rotate_k(0);
+    if (exists(1)) rotate_k(1);
+    __syncthreads();  // rotated tiles visible; table slot 0 free
+    rope_base_fill(2);
+  }
+  __syncthreads();
+  scores(0, s_a);
+  mx_pre = row_max(s_a, 0, std::false_type{});
+
+  // Tiles 0 .. n-3 have an active successor for every wave (a wave's rows
+  // end in tile n-2 or n-1), so the loop takes no tail; the last two tiles
+  // follow it (after moving the scores to s_a when the loop count is odd).
+  int i = 0;
+#pragma unroll 1
+  for (; i + 3 < n; i += 2) {
+    step(i, s_a, s_b, std::false_type{});
+    step(i + 1, s_b, s_a, std::false_type{});
+  }
+  if (n - i == 3) {
+    step(i, s_a, s_b, std::false_type{});
+    ++i;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) s_a[nb] = s_b[nb];
+  }
+  if (n - i == 2) {
+    step(i, s_a, s_b, std::true_type{});
+    last_step(i + 1, s_b);
+  } else {
+    last_step(i, s_a);
+  }
+
+  // ---- epilogue ----
+  const float Mu = m_ref == kNegInf ? 0.f : m_ref;
+  const float l = pair_sum32(l_run);
+  const float inv = l > 0.f ? p.out_scale / l : 0.f;
+  if (qpos < p.S) {
+    const size_t obase = (((size_t)b * p.Hq + head) * p.S + qpos) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r = 4 * g4;
+        store4(p.o, obase + 32 * db + 8 * g4 + 4 * hh, p.out_dtype, acc_o[db][r] * inv, acc_o[db][r + 1] * inv,
+               acc_o[db][r + 2] * inv, acc_o[db][r + 3] * inv);
+      }
+    if (p.lse && hh == 0)
+      p.lse[((size_t)b * p.Hq + head) * p.S + qpos] = l > 0.f ? (Mu + __log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 SIMT kernel: one query row per thread, 64 rows per workgroup.
 // ---------------------------------------------------------------------------
 // cos / sin of angle pos * w_i for the fp32 kernel: the angle is reduced to
@@ -951,6 +1390,24 @@ static void launch_fwd(const PrefillParams& p, bool causal, bool rope, hipStream
   else launch_fwd_h<Tag, D, 2>(p, causal, rope, st);
 }
 
+template <class Tag, int D>
+static void launch_pipe(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
+  const dim3 grid((unsigned)((long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups)), block(256);
+  if (causal) {
+    if (rope) hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, true, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, true, false>), grid, block, 0, st, p);
+  } else {
+    if (rope) hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, false, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, false, false>), grid, block, 0, st, p);
+  }
+}
+
+template <class Tag, int D>
+static void launch_16bit(const PrefillParams& p, int config, bool causal, bool rope, hipStream_t st) {
+  if (config == 2) launch_pipe<Tag, D>(p, causal, rope, st);
+  else launch_fwd<Tag, D>(p, causal, rope, st);
+}
+
 template <class Tag, int D, bool FP8>
 static void launch_mfma(const PrefillParams& p, bool causal, dim3 grid, hipStream_t st) {
   if (causal) hipLaunchKernelGGL((prefill_mfma_kernel<Tag, D, true, false, FP8>), grid, dim3(256), 0, st, p);
@@ -1030,12 +1487,12 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   const bool c = causal != 0;
   switch (in_dtype) {
     case ATTN_BF16:
-      if (D == 64) launch_fwd<Bf16Tag, 64>(p, c, rope, stream);
-      else launch_fwd<Bf16Tag, 128>(p, c, rope, stream);
+      if (D == 64) launch_16bit<Bf16Tag, 64>(p, config, c, rope, stream);
+      else launch_16bit<Bf16Tag, 128>(p, config, c, rope, stream);
       break;
     case ATTN_F16:
-      if (D == 64) launch_fwd<F16Tag, 64>(p, c, rope, stream);
-      else launch_fwd<F16Tag, 128>(p, c, rope, stream);
+      if (D == 64) launch_16bit<F16Tag, 64>(p, config, c, rope, stream);
+      else launch_16bit<F16Tag, 128>(p, config, c, rope, stream);
       break;
     default:  // fp8 e5m2 (RoPE rejected above)
       if (D == 64) launch_mfma<F16Tag, 64, true>(p, c, grid, stream);
@@ -1048,8 +1505,10 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 // Tile configurations of the 16-bit MFMA prefill kernel (fp32 and fp8 inputs
 // have a single configuration):
 //   0 (global default): 4-wave workgroups, 128 query rows, 64-key tiles;
-//   1: 8-wave workgroups whose two halves split the key tiles of 128 rows.
-static const int kPrefillConfigs = 2;
+//   1: 8-wave workgroups whose two halves split the key tiles of 128 rows;
+//   2: the tiling of 0, software-pipelined (S of the next tile overlaps the
+//      softmax of this one).
+static const int kPrefillConfigs = 3;
 
 extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, void* o,
                                              float* lse, int B, int Hq, int Hkv, int S, int D,

@@ -83,14 +83,14 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S):
     assert _maxerr(lse, want_lse) <= 2e-2
 
 
-@pytest.mark.parametrize("config", [0, 1])
+@pytest.mark.parametrize("config", [0, 1, 2])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (4, 2)])
 @pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
                                                   (128, False, True, "f16"), (64, True, True, "bf16")])
 def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype):
     """Every tile configuration of the sweep passes parity before it is timed
     (GQA groups of 4, 1 and 2 query heads: different row layouts per wave)."""
-    assert attn.prefill_num_configs() == 2
+    assert attn.prefill_num_configs() == 3
     q, k, v = prefill_inputs(2, Hq, Hkv, 333, D, dtype, seed=config * 7 + D + Hq)
     theta = 10000.0 if rope else 0.0
     o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
@@ -99,6 +99,23 @@ def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype
                                     return_lse=True)
     assert _maxerr(o, want) <= TOL[dtype]
     assert _maxerr(lse, want_lse) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("S", [1, 40, 64, 65, 128, 129, 192, 257])
+@pytest.mark.parametrize("D,causal,rope,Hq,Hkv", [(128, True, True, 8, 2), (64, False, False, 4, 4),
+                                                  (128, False, False, 4, 1)])
+def test_prefill_tile_counts(attn, S, D, causal, rope, Hq, Hkv):
+    """Sequence lengths giving 1, 2, 3, 4 and 5 key tiles, full and ragged:
+    the pipelined kernel peels its last tile and unrolls the key loop by two,
+    so odd and even tile counts take different code paths."""
+    q, k, v = prefill_inputs(1, Hq, Hkv, S, D, "bf16", seed=S + D)
+    theta = 10000.0 if rope else 0.0
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
+                                   return_lse=True)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta,
+                                    return_lse=True)
+    assert _maxerr(o, want) <= TOL["bf16"]
+    assert _maxerr(lse, want_lse) <= TOL["bf16"]
 
 
 def test_prefill_config_out_of_range(attn):
