@@ -15,6 +15,8 @@ from .ref import (  # noqa: F401
     attention_probs,
     prefill,
     prefill_rows,
+    kv_append,
+    prefill_chunk,
     decode_gqa,
     decode_mla,
     mla_absorb_query,

@@ -163,6 +163,63 @@ def prefill_rows(q, k, v, scale: float, causal: bool, rope_theta: float,
 
 
 # ----------------------------------------------------------------------------
+# Decode neighbours: appending tokens to the static cache, and a chunk of
+# queries against the cache prefix ("Fixed-budget decode audit", "Setup and
+# interpretation": a static append cache; prompts prefilled in chunks of 32)
+# ----------------------------------------------------------------------------
+def kv_append(k_cache, v_cache, kv_len, k_new, v_new, rope_theta: float, q_new=None):
+    """Append T tokens per sequence: k_new, v_new [B,Hkv,T,D] go to slots
+    kv_len[b] .. kv_len[b]+T-1 of the caches [B,Hkv,cap,D].  The slot index is
+    the token's position: K is rotated by it when rope_theta > 0, V is copied.
+    q_new [B,Hq,T,D], if given, is rotated at the same positions.  Returns
+    float64 copies (k_cache, v_cache, kv_len + T, q); slots outside the
+    appended range keep their contents."""
+    k2 = np.array(k_cache, dtype=np.float64)
+    v2 = np.array(v_cache, dtype=np.float64)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    B, _, T, _ = k_new.shape
+    q2 = None if q_new is None else np.array(q_new, dtype=np.float64)
+    for b in range(B):
+        L = int(kv_len[b])
+        pos = L + np.arange(T)
+        kb = rope_rotate(k_new[b], pos, rope_theta) if rope_theta > 0 else k_new[b]
+        k2[b, :, L:L + T] = kb
+        v2[b, :, L:L + T] = v_new[b]
+        if q2 is not None and rope_theta > 0:
+            q2[b] = rope_rotate(q2[b], pos, rope_theta)
+    return k2, v2, np.asarray(kv_len, dtype=np.int64) + T, q2
+
+
+def prefill_chunk(q, k_cache, v_cache, kv_len, scale: float, return_lse: bool = False):
+    """A chunk of T queries per sequence against the cache prefix: q
+    [B,Hq,T,D] (already rotated), caches [B,Hkv,cap,D], kv_len [B] counting
+    the chunk's own tokens.  Row t sits at position p = kv_len[b] - T + t and
+    attends to slots 0..p (causal, aligned at the end of the prefix).  A row
+    with p < 0 sees no key: zero output, lse -inf."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, T, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, T, v_cache.shape[-1]), dtype=np.float64)
+    lse = np.full((B, Hq, T), -np.inf, dtype=np.float64)
+    for b in range(B):
+        L = int(kv_len[b])
+        pos = L - T + np.arange(T)
+        live = pos >= 0
+        if L == 0 or not live.any():
+            continue
+        kb = repeat_kv(np.asarray(k_cache[b:b + 1, :, :L], dtype=np.float64), G)[0]
+        vb = repeat_kv(np.asarray(v_cache[b:b + 1, :, :L], dtype=np.float64), G)[0]
+        for h in range(Hq):
+            t = scale * (q[b, h][live] @ kb[h].T)
+            t = np.where(_causal_mask(pos[live], L), -np.inf, t)
+            out[b, h, live] = softmax(t, axis=-1) @ vb[h]
+            lse[b, h, live] = _logsumexp_rows(t)
+    return (out, lse) if return_lse else out
+
+
+# ----------------------------------------------------------------------------
 # Decode against a static cache
 # ----------------------------------------------------------------------------
 def decode_gqa(q, k_cache, v_cache, kv_len, scale: float):

@@ -333,6 +333,107 @@ def test_combine_splits_handles_all_empty_rows():
 
 
 # ---------------------------------------------------------------------------
+# Decode neighbours: cache append and chunked prefill
+# ---------------------------------------------------------------------------
+def pin_chunked_prefill(mod, S=70, T=32, theta=10000.0, prefix=(0, 9), seed=11):
+    """Prefill a prompt chunk by chunk through kv_append + prefill_chunk (each
+    sequence may already hold a prefix in its cache) and compare every row
+    with the one-shot prefill of the whole sequence.  Returns the max error."""
+    B, Hq, Hkv, D = 2, 4, 2, 8
+    scale = 0.4
+    tot = S + max(prefix)
+    q, k, v = _rand((B, Hq, tot, D), seed), _rand((B, Hkv, tot, D), seed + 1), _rand((B, Hkv, tot, D), seed + 2)
+    cap = tot + 5
+    kc = np.full((B, Hkv, cap, D), np.nan)
+    vc = np.full((B, Hkv, cap, D), np.nan)
+    L = np.zeros(B, dtype=np.int64)
+    err = 0.0
+    # the prefix of sequence b goes in first (one append of its own length per sequence)
+    for b in range(B):
+        if prefix[b]:
+            kb, vb, _, _ = mod.kv_append(kc[b:b + 1], vc[b:b + 1], L[b:b + 1], k[b:b + 1, :, :prefix[b]],
+                                         v[b:b + 1, :, :prefix[b]], theta)
+            kc[b:b + 1], vc[b:b + 1] = kb, vb
+            L[b] = prefix[b]
+    outs = [[] for _ in range(B)]
+    for c0 in range(0, S, T):
+        c1 = min(S, c0 + T)
+        sl = [slice(prefix[b] + c0, prefix[b] + c1) for b in range(B)]
+        kn = np.stack([k[b, :, sl[b]] for b in range(B)])
+        vn = np.stack([v[b, :, sl[b]] for b in range(B)])
+        qn = np.stack([q[b, :, sl[b]] for b in range(B)])
+        kc, vc, L, qr = mod.kv_append(kc, vc, L, kn, vn, theta, qn)
+        o = mod.prefill_chunk(qr, kc, vc, L, scale)
+        for b in range(B):
+            outs[b].append(o[b])
+    for b in range(B):
+        n = prefix[b] + S
+        want = mod.prefill(q[b:b + 1, :, :n], k[b:b + 1, :, :n], v[b:b + 1, :, :n], scale, True, theta)[0]
+        got = np.concatenate(outs[b], axis=1)
+        e = float(np.max(np.abs(got - want[:, prefix[b]:])))
+        err = np.inf if np.isnan(e) else max(err, e)
+    return err
+
+
+@pytest.mark.parametrize("theta,T", [(10000.0, 32), (0.0, 32), (10000.0, 1), (500.0, 17)])
+def test_chunked_prefill_equals_one_shot_prefill(theta, T):
+    """Chunks of 32 (and 1, and 17) over prefixes of 0 and 9 tokens reproduce
+    the one-shot causal RoPE prefill row for row."""
+    assert pin_chunked_prefill(ref, T=T, theta=theta) <= 1e-12
+
+
+def test_decode_equals_chunk_of_one():
+    B, Hq, Hkv, D, cap = 3, 8, 2, 16, 40
+    k = _rand((B, Hkv, cap, D), 21)
+    v = _rand((B, Hkv, cap, D), 22)
+    q = _rand((B, Hq, D), 23)
+    L = np.array([1, 17, 40])
+    want = ref.decode_gqa(q, k, v, L, 0.3)
+    got = ref.prefill_chunk(q[:, :, None], k, v, L, 0.3)[:, :, 0]
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+def test_kv_append_slots_values_and_positions():
+    """Only slots L..L+T-1 change; V is copied bit for bit; with theta = 0 so is
+    K; with RoPE, appending one token at a time gives the same cache as one
+    append of all of them (the slot index is the position)."""
+    B, Hkv, Hq, T, D, cap = 2, 2, 4, 5, 8, 16
+    kc = np.full((B, Hkv, cap, D), np.nan)
+    vc = np.full((B, Hkv, cap, D), np.nan)
+    L = np.array([0, 7])
+    kn, vn, qn = _rand((B, Hkv, T, D), 31), _rand((B, Hkv, T, D), 32), _rand((B, Hq, T, D), 33)
+    k0, v0, L0, q0 = ref.kv_append(kc, vc, L, kn, vn, 0.0, qn)
+    assert np.array_equal(L0, L + T)
+    for b in range(B):
+        assert np.array_equal(k0[b, :, L[b]:L[b] + T], kn[b]) and np.array_equal(v0[b, :, L[b]:L[b] + T], vn[b])
+        outside = np.ones(cap, dtype=bool)
+        outside[L[b]:L[b] + T] = False
+        assert np.all(np.isnan(k0[b][:, outside])) and np.all(np.isnan(v0[b][:, outside]))
+    assert np.array_equal(q0, qn)
+    k1, v1, _, q1 = ref.kv_append(kc, vc, L, kn, vn, 10000.0, qn)
+    ks, vs, Ls = kc, vc, L
+    qs = []
+    for t in range(T):
+        ks, vs, Ls, qt = ref.kv_append(ks, vs, Ls, kn[:, :, t:t + 1], vn[:, :, t:t + 1], 10000.0, qn[:, :, t:t + 1])
+        qs.append(qt)
+    assert np.allclose(k1, ks, atol=1e-14, equal_nan=True) and np.array_equal(v1, vs, equal_nan=True)
+    assert np.allclose(q1, np.concatenate(qs, axis=2), atol=1e-14)
+    # norms are preserved (a rotation) and position 0 is the identity
+    for b in range(B):
+        np.testing.assert_allclose(np.linalg.norm(k1[b, :, L[b]:L[b] + T], axis=-1), np.linalg.norm(kn[b], axis=-1),
+                                   rtol=1e-13)
+    assert np.allclose(k1[0, :, 0], kn[0, :, 0], atol=1e-15)
+
+
+def test_prefill_chunk_rows_without_keys():
+    """kv_len below the chunk length: rows at negative positions see no key."""
+    k, v, q = _rand((1, 1, 8, 4), 41), _rand((1, 1, 8, 4), 42), _rand((1, 1, 5, 4), 43)
+    o, lse = ref.prefill_chunk(q, k, v, np.array([3]), 0.5, return_lse=True)
+    assert np.all(o[0, 0, :2] == 0) and np.all(np.isneginf(lse[0, 0, :2]))
+    assert np.allclose(o[0, 0, 2], v[0, 0, 0])  # position 0 sees only key 0
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each mutant of the oracle must fail at least one pin.
 # ---------------------------------------------------------------------------
 def _mutant_tile_kv(k, G):          # GQA head h -> KV head h % Hkv instead of h // G
@@ -370,6 +471,21 @@ def _mutant_inv_freq(D, theta):                      # exponent i/D instead of 2
     return np.power(float(theta), -np.arange(D // 2) / D)
 
 
+_kv_append_orig = ref.kv_append
+_prefill_chunk_orig = ref.prefill_chunk
+
+
+def _mutant_append_position(k_cache, v_cache, kv_len, k_new, v_new, rope_theta, q_new=None):
+    # K rotated one position too far (slot index + 1)
+    k_new = _rope_rotate_orig(np.asarray(k_new, dtype=np.float64), np.ones(k_new.shape[2]), rope_theta)
+    return _kv_append_orig(k_cache, v_cache, kv_len, k_new, v_new, rope_theta, q_new)
+
+
+def _mutant_chunk_offset(q, k_cache, v_cache, kv_len, scale, return_lse=False):
+    # chunk rows placed one position early (and the last prefix slot dropped)
+    return _prefill_chunk_orig(q, k_cache, v_cache, np.asarray(kv_len) - 1, scale, return_lse)
+
+
 @pytest.mark.parametrize("name,attr,fn,pin", [
     ("gqa-tile", "repeat_kv", _mutant_tile_kv, lambda m: pin_sdpa(m, True)),
     ("rope-interleaved", "rope_rotate", _mutant_rope_interleaved, lambda m: pin_rope_complex(m)),
@@ -378,6 +494,8 @@ def _mutant_inv_freq(D, theta):                      # exponent i/D instead of 2
     ("rope-freq-prefill", "rope_inv_freq", _mutant_inv_freq, lambda m: pin_brute_force(m, True, 10000.0)),
     ("mask-off-by-one", "_causal_mask", _mutant_mask_off_by_one, lambda m: pin_sdpa(m, True)),
     ("merge-flip", "merge_pair", _mutant_merge_flip, lambda m: pin_merge_identity(m)),
+    ("append-position", "kv_append", _mutant_append_position, lambda m: pin_chunked_prefill(m)),
+    ("chunk-offset", "prefill_chunk", _mutant_chunk_offset, lambda m: pin_chunked_prefill(m)),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, attr, fn, pin):
     monkeypatch.setattr(ref, attr, fn)
