@@ -39,6 +39,10 @@ SIGNATURES = {
                                  _c_int, _c_int, _c_float, _vp]),
     "attn_combine_splits": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
     "attn_rope_rotate": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp]),
+    "attn_kv_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_int, _c_float, _c_int, _vp]),
+    "attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_float, _vp]),
 }
 
 

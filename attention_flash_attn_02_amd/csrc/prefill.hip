@@ -58,6 +58,9 @@ struct PrefillParams {
   float rope_flo[64];
   float rope_fmid[64];  // three-way split (f_hi + f_mid + f_lo) for the fp32 kernel
   int halves;  // MFMA kernel: 1 = 4-wave workgroups, 2 = 8-wave split-key workgroups
+  // chunked prefill against a cache prefix (prefill_fwd_kernel<..., CHUNK>)
+  const int* kv_len;  // [B] key lengths including the chunk, device memory
+  int cap;            // cache slots per head
 };
 
 // ---------------------------------------------------------------------------
@@ -445,8 +448,13 @@ __device__ inline float pair_sum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <class Tag, int D, bool CAUSAL, bool ROPE, int HALVES>
+// CHUNK: the queries are a chunk of p.S rows at the end of a cache prefix:
+// K/V rows come from caches with p.cap slots per head, the key length of
+// sequence b is kv_len[b] (read on the device) and query row r sits at
+// position kv_len[b] - p.S + r (causal with that offset).
+template <class Tag, int D, bool CAUSAL, bool ROPE, int HALVES, bool CHUNK = false>
 __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const PrefillParams p) {
+  static_assert(!CHUNK || (CAUSAL && !ROPE && HALVES == 1), "chunk mode: causal, no RoPE, 4 waves");
   constexpr int BN = 64;
   constexpr int ROWB = D * 2;        // bytes per K/V row
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -542,7 +550,10 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
     const int head = kvh * p.G + hg * p.GP + (wq % p.GP);
     const int p0 = ptile * p.P;
     const int pw0 = p0 + (wq / p.GP) * 32;
-    const int kend = CAUSAL ? min(p.S, p0 + p.P) : p.S;
+    // key length and query position offset (plain prefill: S and 0)
+    const int Skv = CHUNK ? min(max(p.kv_len[b], 0), p.cap) : p.S;
+    const int qoff = CHUNK ? Skv - p.S : 0;
+    const int kend = CAUSAL ? max(0, min(Skv, qoff + p0 + p.P)) : Skv;
     const int n_kt = (kend + BN - 1) / BN;
     const int n = (n_kt + HALVES - 1) / HALVES;  // local tiles per half: local i is tile HALVES i + half
     const int qpos = pw0 + m;
@@ -581,7 +592,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
       }
     }
 
-    const size_t kv_row0 = ((size_t)b * p.Hkv + kvh) * p.S;
+    const size_t kv_row0 = ((size_t)b * p.Hkv + kvh) * (CHUNK ? p.cap : p.S);
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k) + kv_row0 * ROWB;
     const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.v) + kv_row0 * ROWB;
     auto exists = [&](int i) { return i >= 0 && i < n && HALVES * i + half < n_kt; };
@@ -595,7 +606,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
     auto tile_rsrc = [&](const uint8_t* src, int i) {
       const int key0 = (HALVES * i + half) * BN;
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src + (size_t)key0 * ROWB), (short)0,
-                                               (p.S - key0) * ROWB, kBufferRsrcWord3);
+                                               (Skv - key0) * ROWB, kBufferRsrcWord3);
     };
     auto dma = [&](const uint8_t* src, uint8_t* dst, const int* loff, int i) {
       const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src, i);
@@ -653,7 +664,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
       }
     };
     auto active = [&](int i) {
-      return exists(i) && !(CAUSAL && (HALVES * i + half) * BN > pw0 + 31);
+      return exists(i) && !(CAUSAL && (HALVES * i + half) * BN > qoff + pw0 + 31);
     };
 
     // ---- running state ----
@@ -723,10 +734,10 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
         // only tiles that cross the diagonal or the end of the sequence are
         // masked; the empty asm keeps this a branch (not per-element selects)
         const int key0 = (HALVES * i + half) * BN;
-        if ((key0 + BN > p.S) || (CAUSAL && key0 + BN - 1 > pw0)) {
+        if ((key0 + BN > Skv) || (CAUSAL && key0 + BN - 1 > qoff + pw0)) {
           asm volatile("" ::: "memory");
           // key = key0 + 4 hh + off(nb, r) is visible iff key <= min(qpos, S - 1)
-          const int lim = (CAUSAL ? min(qpos, p.S - 1) : p.S - 1) - key0 - 4 * hh;
+          const int lim = (CAUSAL ? min(qoff + qpos, Skv - 1) : Skv - 1) - key0 - 4 * hh;
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -741,7 +752,8 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
         mx = pair_max32(mx) * p.scale_log2;
         if (__ballot(mx > m_ref + kLazy)) {
           const float m_new = fmaxf(m_ref, mx);
-          const float alpha = fast_exp2(m_ref - m_new);  // 0 when m_ref = -inf
+          // 0 when m_ref = -inf; 1 for a row that has seen no key yet (both -inf)
+          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_ref - m_new);
           l_run *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
@@ -1100,7 +1112,8 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
   auto softmax_head = [&](float mx) {
     if (__ballot(mx > m_ref + kLazy)) {
       const float m_new = fmaxf(m_ref, mx);
-      const float alpha = fast_exp2(m_ref - m_new);  // 0 when m_ref = -inf
+      // 0 when m_ref = -inf; 1 for a row that has seen no key yet (both -inf)
+      const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_ref - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
@@ -1531,3 +1544,50 @@ extern "C" attn_status attn_prefill_gqa_rope_with_config(
 }
 
 extern "C" int attn_prefill_num_configs(void) { return kPrefillConfigs; }
+
+// ---------------------------------------------------------------------------
+// Chunked prefill against a cache prefix
+// ---------------------------------------------------------------------------
+extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* kv_len, void* o, float* lse, int B, int Hq,
+                                          int Hkv, int T, int D, int cap, attn_dtype dtype,
+                                          attn_dtype out_dtype, float softmax_scale, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !kv_len || !o) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || cap <= 0 || T > cap) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (dtype < ATTN_F32 || dtype > ATTN_FP8_E5M2) return ATTN_ERR_DTYPE;
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_F16 && out_dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 3.0e38f)) return ATTN_ERR_SHAPE;
+  if (!attn_host::aligned(q, 16) || !attn_host::aligned(k_cache, 16) || !attn_host::aligned(v_cache, 16) ||
+      !attn_host::aligned(o, 16) || !attn_host::aligned(kv_len, 4) || (lse && !attn_host::aligned(lse, 4)))
+    return ATTN_ERR_ALIGN;
+  if ((long long)B * Hkv * cap * D > (1LL << 40)) return ATTN_ERR_SHAPE;
+
+  PrefillParams p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.S = T;
+  p.G = Hq / Hkv;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.out_scale = 1.f;
+  p.out_dtype = out_dtype;
+  p.halves = 1;
+  p.kv_len = kv_len;
+  p.cap = cap;
+  p.GP = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+  p.P = 128 / p.GP;
+  p.n_ptiles = (T + p.P - 1) / p.P;
+  p.n_hgroups = p.G / p.GP;
+  const long long items = (long long)p.n_ptiles * B * Hkv * p.n_hgroups;
+  if (items > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  const dim3 grid((unsigned)items), block(256);
+  if (dtype == ATTN_BF16) {
+    if (D == 64) hipLaunchKernelGGL((prefill_fwd_kernel<Bf16Tag, 64, true, false, 1, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_fwd_kernel<Bf16Tag, 128, true, false, 1, true>), grid, block, 0, stream, p);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((prefill_fwd_kernel<F16Tag, 64, true, false, 1, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_fwd_kernel<F16Tag, 128, true, false, 1, true>), grid, block, 0, stream, p);
+  }
+  return attn_host::launch_status();
+}

@@ -92,6 +92,52 @@ def prefill_gqa_rope_unfused(q, k, v, softmax_scale: float, causal: bool = True,
                             return_lse=return_lse, stream=stream, config=config)
 
 
+def kv_append(k_new, v_new, k_cache, v_cache, kv_len, rope_theta: float = 0.0, q=None, advance: bool = True,
+              stream=None):
+    """attn_kv_append: write k_new, v_new [B,Hkv,T,D] into the caches
+    [B,Hkv,cap,D] at slots kv_len[b].., K (and ``q`` [B,Hq,T,D], in place)
+    rotated to those positions when rope_theta > 0; kv_len (int32 [B]) then
+    advances by T unless ``advance`` is False."""
+    B, Hkv, T, D = k_new.shape
+    cap = k_cache.shape[2]
+    if kv_len.dtype != torch.int32 or kv_len.shape != (B,):
+        raise ValueError("kv_len must be int32 [B]")
+    for name, t in (("v_new", v_new),):
+        if t.shape != k_new.shape or t.dtype != k_new.dtype:
+            raise ValueError(f"{name} must match k_new")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.shape != (B, Hkv, cap, D) or t.dtype != k_new.dtype:
+            raise ValueError(f"{name} must be [B,Hkv,cap,D] of k_new's dtype")
+    Hq = 0
+    if q is not None:
+        if q.dim() != 4 or q.shape[0] != B or q.shape[2:] != (T, D) or q.dtype != k_new.dtype:
+            raise ValueError("q must be [B,Hq,T,D] of k_new's dtype")
+        Hq = q.shape[1]
+    _lib.check(_lib.lib().attn_kv_append(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(q, "q") if q is not None else None,
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(kv_len, "kv_len"), B, Hkv, Hq, T, D, cap,
+        _dtype_code(k_new), float(rope_theta), 1 if advance else 0, _stream(stream)))
+    return k_cache, v_cache
+
+
+def prefill_chunk(q, k_cache, v_cache, kv_len, softmax_scale: float, out_dtype=None, out=None,
+                  return_lse: bool = False, stream=None):
+    """attn_prefill_chunk: q [B,Hq,T,D] (rotated) against the cache prefix;
+    kv_len (int32 [B]) counts the chunk's own tokens -> o [B,Hq,T,D]."""
+    B, Hq, T, D = q.shape
+    _, Hkv, cap, _ = k_cache.shape
+    if kv_len.dtype != torch.int32 or kv_len.shape != (B,):
+        raise ValueError("kv_len must be int32 [B]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    _lib.check(_lib.lib().attn_prefill_chunk(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(kv_len, "kv_len"),
+        _dev(out, "out"), _dev(lse, "lse") if lse is not None else None, B, Hq, Hkv, T, D, cap,
+        _dtype_code(q), _dtype_code(out), float(softmax_scale), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
 def decode_gqa_workspace_bytes(B, Hq, cap, D, split=0) -> int:
     return int(_lib.lib().attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split))
 

@@ -202,6 +202,53 @@ attn_status attn_decode_mla(const void* q, const void* kv_cache, const int32_t* 
 attn_status attn_combine_splits(const float* o_part, const float* lse_part, void* o, int R,
                                 int nsplit, int D, attn_dtype out_dtype, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ *
+ * Decode neighbours: the steps on either side of decode attention in a
+ * session with a static append cache ("Fixed-budget decode audit", section
+ * "Setup and interpretation": the cache is appended in place, prompts are
+ * prefilled in chunks of 32).
+ *
+ * attn_kv_append writes T new tokens per sequence into the caches:
+ *   k_new, v_new [B, Hkv, T, D]   dtype
+ *   q            [B, Hq, T, D]    dtype, nullable: the same tokens' queries,
+ *                                 rotated in place when RoPE is on
+ *   k_cache, v_cache [B, Hkv, cap, D]  dtype, written at slots
+ *                                 L .. L+T-1 with L = kv_len[b]
+ *   kv_len       [B] int32 device memory; read on the device (clamped to
+ *                [0, cap]); when `advance` is nonzero it becomes
+ *                min(L + T, cap) after the append.
+ * The slot index is the token's position: K (and q) are rotated as in
+ * attn_prefill_gqa_rope at position L + t when rope_theta > 0; V is copied;
+ * rope_theta <= 0 copies K too.  Tokens whose slot would be >= cap are not
+ * written (precondition: kv_len[b] + T <= cap).  Slots outside the appended
+ * range are not touched.  k_new/v_new must not overlap the caches.
+ * dtype: ATTN_F32, ATTN_F16 or ATTN_BF16; D even, at most 256, half rows a
+ * whole number of 16-byte chunks; with RoPE cap <= 65536.  One kernel, one
+ * workgroup per sequence, enqueued on `stream` (graph-capturable: the
+ * lengths live on the device, so replays keep appending).
+ *
+ * attn_prefill_chunk attends a chunk of T query rows per sequence to the
+ * cache prefix:
+ *   q       [B, Hq, T, D]      dtype (already rotated, e.g. by attn_kv_append)
+ *   k_cache, v_cache [B, Hkv, cap, D]  dtype (K already rotated)
+ *   kv_len  [B] int32 device memory: key count INCLUDING the chunk's own
+ *           tokens (clamped to [0, cap])
+ *   o       [B, Hq, T, D]      out_dtype; lse [B, Hq, T] float32 or NULL
+ * Row t of sequence b sits at position p = kv_len[b] - T + t and attends to
+ * slots 0..p: O = softmax(scale q K^T) V with query head h reading KV head
+ * h / (Hq/Hkv).  Rows with p < 0 have no key and get zeros (lse -inf).
+ * dtype ATTN_BF16 or ATTN_F16 (others: ATTN_ERR_UNSUPPORTED); D 64 or 128;
+ * T <= cap; scale a positive finite number.  One kernel on `stream`.
+ * ------------------------------------------------------------------------ */
+attn_status attn_kv_append(const void* k_new, const void* v_new, void* q, void* k_cache,
+                           void* v_cache, int32_t* kv_len, int B, int Hkv, int Hq, int T, int D,
+                           int cap, attn_dtype dtype, float rope_theta, int advance,
+                           hipStream_t stream);
+attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* kv_len, void* o, float* lse, int B, int Hq,
+                               int Hkv, int T, int D, int cap, attn_dtype dtype,
+                               attn_dtype out_dtype, float softmax_scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,6 +151,31 @@ def test_rope_rejects(lib):
     assert rope(x=P + 8) == 4
 
 
+def test_kv_append_rejects(lib):
+    def app(kn=P, vn=P, q=None, kc=P2, vc=P2, L=P, B=2, Hkv=2, Hq=8, T=1, D=128, cap=64,
+            dt=_lib.ATTN_BF16, theta=10000.0, adv=1):
+        return lib.attn_kv_append(kn, vn, q, kc, vc, L, B, Hkv, Hq, T, D, cap, dt, theta, adv, None)
+    assert app(kn=None) == 1 and app(L=None) == 1
+    assert app(T=0) == 2 and app(cap=0) == 2 and app(D=63) == 2
+    assert app(q=P, Hq=0) == 2
+    assert app(theta=float("nan")) == 2 and app(theta=float("inf")) == 2
+    assert app(dt=_lib.ATTN_FP8_E5M2) == 6 and app(dt=9) == 3
+    assert app(D=258) == 6 and app(cap=70000) == 6
+    assert app(kc=P + 8) == 4 and app(L=P + 2) == 4 and app(q=P + 8) == 4
+
+
+def test_prefill_chunk_rejects(lib):
+    def chunk(q=P, kc=P, vc=P, L=P, o=P2, lse=None, B=2, Hq=16, Hkv=4, T=32, D=128, cap=2056,
+              dt=_lib.ATTN_BF16, odt=_lib.ATTN_BF16, scale=0.088):
+        return lib.attn_prefill_chunk(q, kc, vc, L, o, lse, B, Hq, Hkv, T, D, cap, dt, odt, scale, None)
+    assert chunk(L=None) == 1 and chunk(o=None) == 1
+    assert chunk(T=0) == 2 and chunk(T=3000) == 2 and chunk(Hq=6, Hkv=4) == 2
+    assert chunk(scale=0.0) == 2 and chunk(scale=float("nan")) == 2
+    assert chunk(dt=_lib.ATTN_F32) == 6 and chunk(dt=_lib.ATTN_FP8_E5M2) == 6 and chunk(D=96) == 6
+    assert chunk(odt=_lib.ATTN_FP8_E5M2) == 3 and chunk(dt=8) == 3
+    assert chunk(q=ODD) == 4 and chunk(L=P + 2) == 4 and chunk(lse=P + 2) == 4
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

@@ -382,3 +382,135 @@ def test_combine_matches_pairwise_merge(attn, D, ns, empty):
     got = attn.combine_splits(*_dev(o_part, lse))
     want = oracle.combine_splits(o_part.numpy(), lse.numpy())
     assert _maxerr(got, want) <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# Decode neighbours: cache append and chunked prefill
+# ----------------------------------------------------------------------------
+_REL = {"bf16": 2.0 ** -7, "f16": 2.0 ** -10, "f32": 1e-5}
+
+
+@pytest.mark.parametrize("dtype,D,T,theta", [("bf16", 128, 1, 10000.0), ("bf16", 128, 32, 10000.0),
+                                             ("f16", 64, 17, 500.0), ("f32", 128, 5, 10000.0),
+                                             ("bf16", 128, 32, 0.0)])
+def test_kv_append_matches_oracle(attn, dtype, D, T, theta):
+    """Appended K (rotated at the slot position) and rotated q within one
+    rounding of the element type of the oracle's values, V bit for bit; every
+    other slot keeps its NaN; kv_len advances by T."""
+    B, Hkv, Hq, cap = 3, 4, 16, 2056
+    L = [0, 1000, cap - T]
+    kc = randn((B, Hkv, cap, D), dtype, 61, "k")
+    vc = randn((B, Hkv, cap, D), dtype, 61, "v")
+    kc[:] = float("nan")
+    vc[:] = float("nan")
+    kn, vn = randn((B, Hkv, T, D), dtype, 62, "k"), randn((B, Hkv, T, D), dtype, 62, "v")
+    qn = randn((B, Hq, T, D), dtype, 62, "q")
+    kv_len = torch.tensor(L, dtype=torch.int32)
+    want_k, want_v, want_L, want_q = oracle.kv_append(to_f64(kc), to_f64(vc), L, to_f64(kn), to_f64(vn), theta,
+                                                      to_f64(qn))
+    dkc, dvc, dkn, dvn, dq, dL = _dev(kc, vc, kn, vn, qn, kv_len)
+    attn.kv_append(dkn, dvn, dkc, dvc, dL, rope_theta=theta, q=dq)
+    torch.cuda.synchronize()
+    assert dL.cpu().tolist() == [x + T for x in L]
+    got_k, got_v, got_q = to_f64(dkc), to_f64(dvc), to_f64(dq)
+    for b in range(B):
+        inside = np.zeros(cap, dtype=bool)
+        inside[L[b]:L[b] + T] = True
+        assert np.all(np.isnan(got_k[b][:, ~inside])) and np.all(np.isnan(got_v[b][:, ~inside]))
+        assert np.array_equal(got_v[b][:, inside], to_f64(vn)[b])
+        gk, wk = got_k[b][:, inside], want_k[b][:, inside]
+        assert np.all(np.abs(gk - wk) <= _REL[dtype] * np.maximum(np.abs(wk), 1.0))
+    assert np.all(np.abs(got_q - want_q) <= _REL[dtype] * np.maximum(np.abs(want_q), 1.0))
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,T", [("bf16", 128, 16, 4, 32), ("bf16", 128, 16, 4, 1),
+                                              ("f16", 64, 8, 8, 45), ("bf16", 128, 8, 2, 32),
+                                              ("f16", 128, 4, 4, 130)])
+def test_prefill_chunk_matches_oracle(attn, dtype, D, Hq, Hkv, T):
+    """Chunk rows at positions kv_len - T + t against the cache prefix, with
+    ragged prefixes, NaN in every slot past kv_len (never read) and one
+    sequence shorter than the chunk (its leading rows see no key)."""
+    B, cap = 4, 2056
+    L = [T, 300 + T, cap, max(1, T // 2)]
+    q = randn((B, Hq, T, D), dtype, 71, "q")
+    _, kc, vc, kv_len = decode_gqa_inputs(B, Hq, Hkv, D, cap, 0, dtype, seed=72, nan_tail=True, lengths=L)
+    o, lse = attn.prefill_chunk(*_dev(q, kc, vc, kv_len), 1 / math.sqrt(D), return_lse=True)
+    want, want_lse = oracle.prefill_chunk(to_f64(q), to_f64(kc), to_f64(vc), L, 1 / math.sqrt(D), return_lse=True)
+    assert _maxerr(o, want) <= TOL[dtype]
+    got_lse = to_f64(lse)
+    dead = np.isneginf(want_lse)
+    assert np.array_equal(np.isneginf(got_lse), dead)
+    assert np.max(np.abs(got_lse[~dead] - want_lse[~dead])) <= TOL[dtype]
+
+
+def test_chunked_prefill_pipeline_equals_fused_prefill(attn):
+    """The C2 prompt (S=300 here) prefilled chunk by chunk (kv_append with
+    RoPE, then prefill_chunk per 32-row chunk) against the oracle's one-shot
+    causal RoPE prefill and against the fused GPU prefill."""
+    B, Hq, Hkv, S, D, T, cap = 1, 32, 8, 300, 128, 32, 320
+    q, k, v = prefill_inputs(B, Hq, Hkv, S, D, "bf16", seed=81)
+    scale = 1 / math.sqrt(D)
+    dq, dk, dv = _dev(q, k, v)
+    fused = attn.prefill_gqa_rope(dq, dk, dv, scale, causal=True, rope_theta=10000.0)
+    kc = torch.full((B, Hkv, cap, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    kv_len = torch.zeros(B, dtype=torch.int32, device="cuda")
+    outs = []
+    for c0 in range(0, S, T):
+        c1 = min(S, c0 + T)
+        qc = dq[:, :, c0:c1].contiguous()
+        attn.kv_append(dk[:, :, c0:c1].contiguous(), dv[:, :, c0:c1].contiguous(), kc, vc, kv_len,
+                       rope_theta=10000.0, q=qc)
+        outs.append(attn.prefill_chunk(qc, kc, vc, kv_len, scale))
+    got = torch.cat(outs, dim=2)
+    assert kv_len.item() == S
+    want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), scale, True, 10000.0)
+    assert _maxerr(got, want) <= TOL["bf16"]
+    assert _maxerr(got, to_f64(fused)) <= TOL["bf16"]
+
+
+def test_decode_step_graph_appends_and_attends(attn):
+    """A decode step (kv_append with advance, then decode_gqa) captured once in
+    a hipGraph and replayed: each replay appends the next token at the slot
+    kv_len names and attends to it (eager steps give the same outputs)."""
+    B, Hq, Hkv, D, cap, L0, steps = 4, 16, 4, 128, 2056, 1000, 3
+    scale = 1 / math.sqrt(D)
+    _, kc, vc, _ = decode_gqa_inputs(B, Hq, Hkv, D, cap, L0, "bf16", seed=91)
+    toks = [(randn((B, Hkv, 1, D), "bf16", 92 + s, "k"), randn((B, Hkv, 1, D), "bf16", 92 + s, "v"),
+             randn((B, Hq, 1, D), "bf16", 92 + s, "q")) for s in range(steps)]
+    # eager reference run
+    ekc, evc = kc.cuda(), vc.cuda()
+    eL = torch.full((B,), L0, dtype=torch.int32, device="cuda")
+    eager = []
+    for kn, vn, qn in toks:
+        qd = qn.cuda()
+        attn.kv_append(kn.cuda(), vn.cuda(), ekc, evc, eL, rope_theta=10000.0, q=qd)
+        eager.append(attn.decode_gqa(qd[:, :, 0].contiguous(), ekc, evc, eL, scale).clone())
+    # graph: static input buffers refilled between replays
+    gkc, gvc = kc.cuda(), vc.cuda()
+    gL = torch.full((B,), L0, dtype=torch.int32, device="cuda")
+    skn, svn = torch.empty_like(toks[0][0], device="cuda"), torch.empty_like(toks[0][1], device="cuda")
+    sq = torch.empty_like(toks[0][2], device="cuda")
+    sq1 = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(attn.decode_gqa_workspace_bytes(B, Hq, cap, D), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            attn.kv_append(skn, svn, gkc, gvc, gL, rope_theta=10000.0, q=sq)
+            sq1.copy_(sq[:, :, 0])
+            attn.decode_gqa(sq1, gkc, gvc, gL, scale, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    # capture only enqueued: the caches and lengths are still untouched
+    assert torch.equal(gL.cpu(), torch.full((B,), L0, dtype=torch.int32))
+    for step, (kn, vn, qn) in enumerate(toks):
+        skn.copy_(kn)
+        svn.copy_(vn)
+        sq.copy_(qn)
+        g.replay()
+        torch.cuda.synchronize()
+        assert gL.cpu().tolist() == [L0 + step + 1] * B
+        assert torch.equal(out, eager[step])
+    assert torch.equal(gkc, ekc) and torch.equal(gvc, evc)
