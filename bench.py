@@ -185,6 +185,66 @@ def rope_factorial(graph_steps=20, iters=50):
     return out
 
 
+def decode_neighbours(iters=50):
+    """The steps on either side of decode attention: (1) a decode step of the
+    GQA decode workload (B=128) with the new token appended first
+    (attn_kv_append with RoPE, then attn_decode_gqa), and the append alone;
+    (2) the causal GQA RoPE prefill prompt (S=2048) prefilled in chunks of 32
+    (append the chunk with RoPE, then attn_prefill_chunk) against the one-shot
+    fused prefill.  hipGraph replay, warm."""
+    import torch
+    import attention_flash_attn_02_amd as attn
+    from workloads import decode_gqa_inputs, prefill_inputs, randn
+    dev = torch.device("cuda:0")
+    out = {}
+    B, Hq, Hkv, D, cap = 128, 16, 4, 128, 2056
+    scale = 1 / math.sqrt(D)
+    q, kc, vc, L = [t.to(dev) for t in decode_gqa_inputs(B, Hq, Hkv, D, cap, 2048, "bf16")]
+    L_app = L - 1  # the new token goes to slot 2047, decode then attends 2048 keys
+    kn = randn((B, Hkv, 1, D), "bf16", 5, "k").to(dev)
+    vn = randn((B, Hkv, 1, D), "bf16", 5, "v").to(dev)
+    qn = q.view(B, Hq, 1, D)
+    o = torch.empty_like(q)
+    ws = torch.empty(attn.decode_gqa_workspace_bytes(B, Hq, cap, D), dtype=torch.uint8, device=dev)
+    app = lambda: attn.kv_append(kn, vn, kc, vc, L_app, rope_theta=10000.0, q=qn, advance=False)  # noqa: E731
+
+    def step():
+        app()
+        attn.decode_gqa(q, kc, vc, L, scale, out=o, workspace=ws)
+    ma = time_graph(app, 20, 5)
+    ms = time_graph(step, 20, 5)
+    by = gqa_decode_bytes(B)
+    out["decode_step_B128"] = {"append_us": round(ma * 1e3, 2), "append_plus_decode_us": round(ms * 1e3, 2),
+                               "decode_bytes": by, "step_GBs": round(by / (ms * 1e-3) / 1e9, 1)}
+    del q, kc, vc, L, o, ws
+    B, Hq, Hkv, S, D, T = 1, 32, 8, 2048, 128, 32
+    scale = 1 / math.sqrt(D)
+    q, k, v = [t.to(dev) for t in prefill_inputs(B, Hq, Hkv, S, D, "bf16")]
+    chunks = [(q[:, :, c:c + T].contiguous(), k[:, :, c:c + T].contiguous(), v[:, :, c:c + T].contiguous())
+              for c in range(0, S, T)]
+    qb = [c[0].clone() for c in chunks]  # rotated in place each run: restored from chunks first
+    kc = torch.empty((B, Hkv, S, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    Lc = torch.zeros(B, dtype=torch.int32, device=dev)
+    oc = [torch.empty_like(c[0]) for c in chunks]
+
+    def chunked():
+        Lc.zero_()
+        for (qc, kk, vv), qr, oo in zip(chunks, qb, oc):
+            qr.copy_(qc)
+            attn.kv_append(kk, vv, kc, vc, Lc, rope_theta=10000.0, q=qr)
+            attn.prefill_chunk(qr, kc, vc, Lc, scale, out=oo)
+    fo = torch.empty_like(q)
+    mc = time_graph(chunked, 1, 5)
+    mf = time_graph(lambda: attn.prefill_gqa_rope(q, k, v, scale, causal=True, rope_theta=10000.0, out=fo), 20, 5)
+    flops = prefill_flops(B, Hq, S, D, True)
+    out["chunked_prefill_S2048_T32"] = {"chunked_us": round(mc * 1e3, 2), "one_shot_fused_us": round(mf * 1e3, 2),
+                                        "chunked_tflops": round(flops / (mc * 1e-3) / 1e12, 1),
+                                        "chunks": len(chunks)}
+    torch.cuda.empty_cache()
+    return out
+
+
 def sweep(scale):
     """Every tile configuration per shape; gap of the global configuration to the best one.
 
@@ -410,6 +470,8 @@ def main():
         sec["decode_mla"] = mla
         sec["rope_fusion_factorial"] = rope_factorial()
         log("rope fusion:", json.dumps(sec["rope_fusion_factorial"]))
+        sec["decode_neighbours"] = decode_neighbours()
+        log("decode neighbours:", json.dumps(sec["decode_neighbours"]))
         if not args.no_sweep:
             sec["sweep"] = sweep(scale)
             log("sweep:", json.dumps(sec["sweep"]))
