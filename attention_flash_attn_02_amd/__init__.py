@@ -16,6 +16,7 @@ from .ops import (  # noqa: F401
     decode_mla_workspace_bytes,
     kv_append,
     prefill_chunk,
+    prefill_chunk_workspace_bytes,
     prefill_gqa_rope,
     prefill_gqa_rope_unfused,
     prefill_num_configs,

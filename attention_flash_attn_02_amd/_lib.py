@@ -41,8 +41,9 @@ SIGNATURES = {
     "attn_rope_rotate": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp]),
     "attn_kv_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 _c_int, _c_float, _c_int, _vp]),
-    "attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                    _c_int, _c_int, _c_int, _c_float, _vp]),
+    "attn_prefill_chunk_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp]),
 }
 
 

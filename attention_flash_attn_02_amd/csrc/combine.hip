@@ -20,8 +20,8 @@ namespace attn {
 // of every split with independent loads.  Requires D % 4 == 0.
 __global__ __launch_bounds__(256) void combine_kernel_v4(const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part,
-                                                         void* __restrict__ o, int R, int nsplit, int D,
-                                                         int out_dtype) {
+                                                         void* __restrict__ o, float* __restrict__ lse_out,
+                                                         int R, int nsplit, int D, int out_dtype) {
   const int d4n = D >> 2;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   if (t >= (long long)R * d4n) return;
@@ -32,6 +32,7 @@ __global__ __launch_bounds__(256) void combine_kernel_v4(const float* __restrict
   const size_t oidx = (size_t)r * D + d;
   if (mx == kNegInf) {
     store4(o, oidx, out_dtype, 0.f, 0.f, 0.f, 0.f);
+    if (lse_out && d == 0) lse_out[r] = kNegInf;
     return;
   }
   const f32x4* op = reinterpret_cast<const f32x4*>(o_part + (size_t)r * nsplit * D + d);
@@ -56,6 +57,7 @@ __global__ __launch_bounds__(256) void combine_kernel_v4(const float* __restrict
   }
   const float inv = 1.f / wsum;
   store4(o, oidx, out_dtype, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  if (lse_out && d == 0) lse_out[r] = mx + __log2f(wsum) * kLn2;
 }
 
 // General D: one wave per row, four rows per workgroup.  Lane s holds split
@@ -64,8 +66,8 @@ __global__ __launch_bounds__(256) void combine_kernel_v4(const float* __restrict
 // loads.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
-                                                      void* __restrict__ o, int R, int nsplit, int D,
-                                                      int out_dtype) {
+                                                      void* __restrict__ o, float* __restrict__ lse_out,
+                                                      int R, int nsplit, int D, int out_dtype) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= R) return;
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const size_t obase = (size_t)r * D;
   if (mx == kNegInf) {
     for (int d = lane; d < D; d += 64) store1(o, obase + d, out_dtype, 0.f);
+    if (lse_out && lane == 0) lse_out[r] = kNegInf;
     return;
   }
   float wsum = 0.f;
@@ -84,6 +87,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
   const float inv = 1.f / wsum;
+  if (lse_out && lane == 0) lse_out[r] = mx + __log2f(wsum) * kLn2;
   const float* op = o_part + (size_t)r * nsplit * D;
   for (int d0 = 0; d0 < D; d0 += 64) {
     const int d = d0 + lane;
@@ -109,14 +113,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
-                    int out_dtype, hipStream_t stream) {
+                    int out_dtype, hipStream_t stream, float* lse_out) {
   if (D % 4 == 0) {
     const long long threads = (long long)R * (D / 4);
     hipLaunchKernelGGL(combine_kernel_v4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                       o_part, lse_part, o, R, nsplit, D, out_dtype);
+                       o_part, lse_part, o, lse_out, R, nsplit, D, out_dtype);
   } else {
-    hipLaunchKernelGGL(combine_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, o_part, lse_part, o, R,
-                       nsplit, D, out_dtype);
+    hipLaunchKernelGGL(combine_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, o_part, lse_part, o, lse_out,
+                       R, nsplit, D, out_dtype);
   }
 }
 

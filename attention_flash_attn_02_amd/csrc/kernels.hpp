@@ -6,9 +6,10 @@
 namespace attn {
 
 // Merge split partials o_part [R, nsplit, D] / lse_part [R, nsplit] into
-// o [R, D] (out_dtype) on `stream`.
+// o [R, D] (out_dtype) on `stream`; lse_out [R] (natural log), if given,
+// receives the merged log-sum-exp.
 void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
-                    int out_dtype, hipStream_t stream);
+                    int out_dtype, hipStream_t stream, float* lse_out = nullptr);
 
 // Workspace layout of the decode calls: partial outputs first, then the
 // partial log-sum-exps, each 256-byte aligned.

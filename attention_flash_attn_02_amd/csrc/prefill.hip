@@ -30,6 +30,7 @@
 // fp32 inputs use a plain SIMT kernel (one query row per thread).
 
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace attn {
 
@@ -61,6 +62,10 @@ struct PrefillParams {
   // chunked prefill against a cache prefix (prefill_fwd_kernel<..., CHUNK>)
   const int* kv_len;  // [B] key lengths including the chunk, device memory
   int cap;            // cache slots per head
+  int nsplit;         // key ranges per item (1: results go straight to o / lse)
+  int split_keys;     // keys per range, a multiple of 64
+  float* ws_o;        // [B*Hq*S, nsplit, D] partial outputs (nsplit > 1)
+  float* ws_lse;      // [B*Hq*S, nsplit] partial log-sum-exps (nsplit > 1)
 };
 
 // ---------------------------------------------------------------------------
@@ -504,7 +509,8 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
   }
 
   const int per_ptile = p.B * p.Hkv * p.n_hgroups;
-  const int n_items = p.n_ptiles * per_ptile;
+  // (chunk mode: every item is further split into p.nsplit key ranges)
+  const int n_items = p.n_ptiles * per_ptile * (CHUNK ? p.nsplit : 1);
   // causal, 8 waves: this workgroup takes long item k and short item n-1-k.
   // 4 waves: one item; the second half of the grid takes the short items in
   // reverse order, so that workgroups k and k + n/2 (which tend to share a CU
@@ -540,7 +546,9 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
 #pragma unroll 1
   for (int itn = 0; itn < n_my; ++itn) {
     if (itn > 0) __syncthreads();  // LDS of the previous item is free
-    const int item = itn == 0 ? item_long : item_short;
+    const int item_ks = itn == 0 ? item_long : item_short;
+    const int split = CHUNK ? item_ks % p.nsplit : 0;  // key range of this item
+    const int item = CHUNK ? item_ks / p.nsplit : item_ks;
     const int ptile = p.n_ptiles - 1 - item / per_ptile;
     int rest = item % per_ptile;
     const int hg = rest % p.n_hgroups;
@@ -553,8 +561,13 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
     // key length and query position offset (plain prefill: S and 0)
     const int Skv = CHUNK ? min(max(p.kv_len[b], 0), p.cap) : p.S;
     const int qoff = CHUNK ? Skv - p.S : 0;
-    const int kend = CAUSAL ? max(0, min(Skv, qoff + p0 + p.P)) : Skv;
-    const int n_kt = (kend + BN - 1) / BN;
+    const int kend_all = CAUSAL ? max(0, min(Skv, qoff + p0 + p.P)) : Skv;
+    // key range [kbeg, kend) of this item: all keys, or (chunk mode) split
+    // `split` of p.split_keys keys (a multiple of the 64-key tile)
+    const int kbeg = CHUNK ? split * p.split_keys : 0;
+    const int kend = CHUNK ? min(kend_all, kbeg + p.split_keys) : kend_all;
+    const int t0 = kbeg / BN;  // first key tile
+    const int n_kt = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
     const int n = (n_kt + HALVES - 1) / HALVES;  // local tiles per half: local i is tile HALVES i + half
     const int qpos = pw0 + m;
 
@@ -604,7 +617,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
     // as zero without a memory access (those keys are masked and their
     // probabilities are exactly 0); all address arithmetic is scalar.
     auto tile_rsrc = [&](const uint8_t* src, int i) {
-      const int key0 = (HALVES * i + half) * BN;
+      const int key0 = (t0 + HALVES * i + half) * BN;
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src + (size_t)key0 * ROWB), (short)0,
                                                (Skv - key0) * ROWB, kBufferRsrcWord3);
     };
@@ -631,7 +644,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
     // constants, and the two are combined by the angle-addition formulas.
     auto rope_base_fill = [&](int i) {
       if (wq == 0 && lane < HALF) {
-        const float key0 = (float)((HALVES * i + half) * BN);
+        const float key0 = (float)((t0 + HALVES * i + half) * BN);
         const float rev = __builtin_amdgcn_fractf(key0 * fhi_lane) + key0 * flo_lane;
         rope_base[half][i & 1][lane] = __builtin_amdgcn_cosf(rev);
         rope_base[half][i & 1][HALF + lane] = __builtin_amdgcn_sinf(rev);
@@ -664,7 +677,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
       }
     };
     auto active = [&](int i) {
-      return exists(i) && !(CAUSAL && (HALVES * i + half) * BN > qoff + pw0 + 31);
+      return exists(i) && !(CAUSAL && (t0 + HALVES * i + half) * BN > qoff + pw0 + 31);
     };
 
     // ---- running state ----
@@ -733,7 +746,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
         // ---- mask, lazy online softmax ----
         // only tiles that cross the diagonal or the end of the sequence are
         // masked; the empty asm keeps this a branch (not per-element selects)
-        const int key0 = (HALVES * i + half) * BN;
+        const int key0 = (t0 + HALVES * i + half) * BN;
         if ((key0 + BN > Skv) || (CAUSAL && key0 + BN - 1 > qoff + pw0)) {
           asm volatile("" ::: "memory");
           // key = key0 + 4 hh + off(nb, r) is visible iff key <= min(qpos, S - 1)
@@ -823,8 +836,15 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
       const float f0 = fast_exp2(m_ref - Mu), f1 = fast_exp2(m1 - Mu);
       const float l = pair_sum32(l_run * f0 + l1 * f1);
       const float inv = l > 0.f ? p.out_scale / l : 0.f;
+      // chunk mode with several key ranges: this item's result (normalised
+      // within its range) and its log-sum-exp go to the split workspace
+      // [rows, nsplit, D] / [rows, nsplit] for the combine step
+      const bool to_ws = CHUNK && p.nsplit > 1;
+      const size_t row = ((size_t)b * p.Hq + head) * p.S + qpos;
       if (qpos < p.S) {
-        const size_t obase = (((size_t)b * p.Hq + head) * p.S + qpos) * D;
+        const size_t obase = to_ws ? (row * p.nsplit + split) * D : row * D;
+        void* const obuf = to_ws ? static_cast<void*>(p.ws_o) : p.o;
+        const int odt = to_ws ? (int)ATTN_F32 : p.out_dtype;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -835,10 +855,11 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
               const int r = 4 * g4 + e;
               v4[e] = (HALVES == 2 ? acc_o[db][r] * f0 + sc[(db * 16 + r) * 64 + lane] * f1 : acc_o[db][r]) * inv;
             }
-            store4(p.o, obase + 32 * db + 8 * g4 + 4 * hh, p.out_dtype, v4[0], v4[1], v4[2], v4[3]);
+            store4(obuf, obase + 32 * db + 8 * g4 + 4 * hh, odt, v4[0], v4[1], v4[2], v4[3]);
           }
-        if (p.lse && hh == 0)
-          p.lse[((size_t)b * p.Hq + head) * p.S + qpos] = l > 0.f ? (Mu + __log2f(l)) * kLn2 : kNegInf;
+        const float lse_row = l > 0.f ? (Mu + __log2f(l)) * kLn2 : kNegInf;
+        if (to_ws && hh == 0) p.ws_lse[row * p.nsplit + split] = lse_row;
+        else if (p.lse && hh == 0) p.lse[row] = lse_row;
       }
     }
   }
@@ -1548,13 +1569,37 @@ extern "C" int attn_prefill_num_configs(void) { return kPrefillConfigs; }
 // ---------------------------------------------------------------------------
 // Chunked prefill against a cache prefix
 // ---------------------------------------------------------------------------
+// Keys per split: `split` if positive, else enough ranges that the launch has
+// about 512 workgroups, with at least 256 keys per range (shorter ranges cost
+// more in partial-result traffic than they gain in parallelism).
+static int chunk_split_keys(int B, int Hq, int Hkv, int T, int cap, int split) {
+  if (split > 0) return split;
+  const int G = Hq / Hkv, GP = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const long long base = (long long)((T + 128 / GP - 1) / (128 / GP)) * B * Hkv * (G / GP);
+  const long long want = (512 + base - 1) / base;
+  long long keys = (cap + want - 1) / want;
+  keys = (keys + 63) / 64 * 64;
+  return (int)(keys < 256 ? 256 : keys);
+}
+
+extern "C" size_t attn_prefill_chunk_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int cap, int split) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || cap <= 0 || Hq % Hkv != 0) return 0;
+  const int sk = chunk_split_keys(B, Hq, Hkv, T, cap, split);
+  if (sk <= 0) return 0;
+  const long long nsplit = (cap + sk - 1) / sk;
+  if (nsplit <= 1) return 0;
+  return split_workspace((long long)B * Hq * T, nsplit, D).total;
+}
+
 extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
-                                          const int32_t* kv_len, void* o, float* lse, int B, int Hq,
-                                          int Hkv, int T, int D, int cap, attn_dtype dtype,
-                                          attn_dtype out_dtype, float softmax_scale, hipStream_t stream) {
+                                          const int32_t* kv_len, void* o, float* lse, void* workspace,
+                                          size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D,
+                                          int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
+                                          float softmax_scale, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !kv_len || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || cap <= 0 || T > cap) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (split > 0 && (split % 64 != 0)) return ATTN_ERR_SHAPE;
   if (dtype < ATTN_F32 || dtype > ATTN_FP8_E5M2) return ATTN_ERR_DTYPE;
   if (out_dtype != ATTN_F32 && out_dtype != ATTN_F16 && out_dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
@@ -1563,7 +1608,18 @@ extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, co
   if (!attn_host::aligned(q, 16) || !attn_host::aligned(k_cache, 16) || !attn_host::aligned(v_cache, 16) ||
       !attn_host::aligned(o, 16) || !attn_host::aligned(kv_len, 4) || (lse && !attn_host::aligned(lse, 4)))
     return ATTN_ERR_ALIGN;
-  if ((long long)B * Hkv * cap * D > (1LL << 40)) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hkv * cap * D > (1LL << 40) || (long long)B * Hq * T * D > (1LL << 40)) return ATTN_ERR_SHAPE;
+
+  const int sk = chunk_split_keys(B, Hq, Hkv, T, cap, split);
+  const int nsplit = (cap + sk - 1) / sk;
+  const long long R = (long long)B * Hq * T;
+  SplitWorkspace w{};
+  if (nsplit > 1) {
+    w = split_workspace(R, nsplit, D);
+    if (!workspace || workspace_bytes < w.total) return ATTN_ERR_WORKSPACE;
+    if (!attn_host::aligned(workspace, 256)) return ATTN_ERR_ALIGN;
+    if (R > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  }
 
   PrefillParams p{};
   p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
@@ -1575,11 +1631,17 @@ extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, co
   p.halves = 1;
   p.kv_len = kv_len;
   p.cap = cap;
+  p.nsplit = nsplit;
+  p.split_keys = sk;
+  if (nsplit > 1) {
+    p.ws_o = reinterpret_cast<float*>(workspace);
+    p.ws_lse = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + w.lse_offset);
+  }
   p.GP = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
   p.P = 128 / p.GP;
   p.n_ptiles = (T + p.P - 1) / p.P;
   p.n_hgroups = p.G / p.GP;
-  const long long items = (long long)p.n_ptiles * B * Hkv * p.n_hgroups;
+  const long long items = (long long)p.n_ptiles * B * Hkv * p.n_hgroups * nsplit;
   if (items > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   const dim3 grid((unsigned)items), block(256);
   if (dtype == ATTN_BF16) {
@@ -1589,5 +1651,6 @@ extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, co
     if (D == 64) hipLaunchKernelGGL((prefill_fwd_kernel<F16Tag, 64, true, false, 1, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((prefill_fwd_kernel<F16Tag, 128, true, false, 1, true>), grid, block, 0, stream, p);
   }
+  if (nsplit > 1) launch_combine(p.ws_o, p.ws_lse, o, (int)R, nsplit, D, out_dtype, stream, lse);
   return attn_host::launch_status();
 }

@@ -103,8 +103,10 @@ __global__ __launch_bounds__(256) void rope_kernel(const RopeParams p) {
 // of sequence b go to slots L .. L+T-1 with L = kv_len[b]; the slot index is
 // the token's position, K is rotated to it (rope on), V is copied, and the
 // queries of the same tokens are rotated in place at the same positions.
-// One workgroup per sequence: every thread reads L before the barrier that
-// precedes the (optional) update kv_len[b] = min(L + T, cap).
+// gridDim.y workgroups per sequence share its rows.  With one workgroup per
+// sequence the update kv_len[b] = min(L + T, cap) follows a barrier after
+// which every thread has read L; with several, advance_kernel does it as a
+// second launch (stream order puts it after every read).
 // ---------------------------------------------------------------------------
 struct AppendParams {
   const void* k_new;  // [B, Hkv, T, D]
@@ -128,12 +130,13 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   const int half = p.D / 2, cpr = half / EPC, cpf = p.D / EPC;  // chunk pairs / chunks per row
   const int L = min(max(p.kv_len[b], 0), p.cap);
   const size_t rowb = (size_t)p.D * EB;
+  const int w0 = blockIdx.y * 256 + threadIdx.x, ws = 256 * gridDim.y;
   const uint8_t* kn = reinterpret_cast<const uint8_t*>(p.k_new) + (size_t)b * p.Hkv * p.T * rowb;
   const uint8_t* vn = reinterpret_cast<const uint8_t*>(p.v_new) + (size_t)b * p.Hkv * p.T * rowb;
   uint8_t* kc = reinterpret_cast<uint8_t*>(p.k_cache) + (size_t)b * p.Hkv * p.cap * rowb;
   uint8_t* vc = reinterpret_cast<uint8_t*>(p.v_cache) + (size_t)b * p.Hkv * p.cap * rowb;
   // K: rows (h, t) x chunk pairs
-  for (int w = threadIdx.x; w < p.Hkv * p.T * cpr; w += 256) {
+  for (int w = w0; w < p.Hkv * p.T * cpr; w += ws) {
     const int row = w / cpr, c = w % cpr, h = row / p.T, t = row % p.T;
     const int slot = L + t;
     if (slot >= p.cap) continue;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
     *reinterpret_cast<u32x4*>(dst + half * EB + 16 * c) = hi;
   }
   // V: rows (h, t) x chunks, copied
-  for (int w = threadIdx.x; w < p.Hkv * p.T * cpf; w += 256) {
+  for (int w = w0; w < p.Hkv * p.T * cpf; w += ws) {
     const int row = w / cpf, c = w % cpf, h = row / p.T, t = row % p.T;
     const int slot = L + t;
     if (slot >= p.cap) continue;
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   // Q: rows (h, t) x chunk pairs, rotated in place at position L + t
   if (p.q && p.rope) {
     uint8_t* qb = reinterpret_cast<uint8_t*>(p.q) + (size_t)b * p.Hq * p.T * rowb;
-    for (int w = threadIdx.x; w < p.Hq * p.T * cpr; w += 256) {
+    for (int w = w0; w < p.Hq * p.T * cpr; w += ws) {
       const int row = w / cpr, c = w % cpr, t = row % p.T;
       uint8_t* x = qb + (size_t)row * rowb;
       u32x4 lo = *reinterpret_cast<const u32x4*>(x + 16 * c);
@@ -166,10 +169,15 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
       *reinterpret_cast<u32x4*>(x + half * EB + 16 * c) = hi;
     }
   }
-  if (p.advance) {
+  if (p.advance && gridDim.y == 1) {
     __syncthreads();  // every thread has read kv_len[b]
     if (threadIdx.x == 0) p.kv_len[b] = min(L + p.T, p.cap);
   }
+}
+
+__global__ __launch_bounds__(256) void advance_kernel(int* kv_len, int B, int T, int cap) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b < B) kv_len[b] = min(max(kv_len[b], 0) + T, cap);
 }
 
 }  // namespace attn
@@ -232,9 +240,14 @@ extern "C" attn_status attn_kv_append(const void* k_new, const void* v_new, void
   p.rope = rope ? 1 : 0;
   p.advance = advance ? 1 : 0;
   if (rope) attn_host::rope_freq_split(rope_theta, D, nullptr, p.rope_fhi, p.rope_flo, p.rope_fmid);
-  const dim3 grid((unsigned)B), block(256);
+  // workgroups per sequence: about 256 rotated chunk pairs each (one per thread)
+  const long long pairs = (long long)(Hkv + p.Hq) * T * ((D / 2) * eb / 16);
+  const long long gy = (pairs + 255) / 256;
+  const dim3 grid((unsigned)B, (unsigned)(gy < 1 ? 1 : gy > 1024 ? 1024 : gy)), block(256);
   if (dtype == ATTN_BF16) hipLaunchKernelGGL((append_kernel<Bf16Tag>), grid, block, 0, stream, p);
   else if (dtype == ATTN_F16) hipLaunchKernelGGL((append_kernel<F16Tag>), grid, block, 0, stream, p);
   else hipLaunchKernelGGL((append_kernel<F32Elem>), grid, block, 0, stream, p);
+  if (advance && grid.y > 1)
+    hipLaunchKernelGGL(advance_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, kv_len, B, T, cap);
   return attn_host::launch_status();
 }

@@ -120,10 +120,16 @@ def kv_append(k_new, v_new, k_cache, v_cache, kv_len, rope_theta: float = 0.0, q
     return k_cache, v_cache
 
 
+def prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split=0) -> int:
+    return int(_lib.lib().attn_prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split))
+
+
 def prefill_chunk(q, k_cache, v_cache, kv_len, softmax_scale: float, out_dtype=None, out=None,
-                  return_lse: bool = False, stream=None):
+                  return_lse: bool = False, split: int = 0, workspace=None, stream=None):
     """attn_prefill_chunk: q [B,Hq,T,D] (rotated) against the cache prefix;
-    kv_len (int32 [B]) counts the chunk's own tokens -> o [B,Hq,T,D]."""
+    kv_len (int32 [B]) counts the chunk's own tokens -> o [B,Hq,T,D].  The
+    key ranges of ``split`` keys (0: default) use ``workspace`` (allocated if
+    not given and needed)."""
     B, Hq, T, D = q.shape
     _, Hkv, cap, _ = k_cache.shape
     if kv_len.dtype != torch.int32 or kv_len.shape != (B,):
@@ -131,10 +137,15 @@ def prefill_chunk(q, k_cache, v_cache, kv_len, softmax_scale: float, out_dtype=N
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    need = prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(_lib.lib().attn_prefill_chunk(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(kv_len, "kv_len"),
-        _dev(out, "out"), _dev(lse, "lse") if lse is not None else None, B, Hq, Hkv, T, D, cap,
-        _dtype_code(q), _dtype_code(out), float(softmax_scale), _stream(stream)))
+        _dev(out, "out"), _dev(lse, "lse") if lse is not None else None, ws_ptr, ws_bytes, B, Hq, Hkv, T, D,
+        cap, int(split), _dtype_code(q), _dtype_code(out), float(softmax_scale), _stream(stream)))
     return (out, lse) if return_lse else out
 
 

@@ -227,13 +227,15 @@ def decode_neighbours(iters=50):
     vc = torch.empty_like(kc)
     Lc = torch.zeros(B, dtype=torch.int32, device=dev)
     oc = [torch.empty_like(c[0]) for c in chunks]
+    wsc = torch.empty(max(1, attn.prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, S)), dtype=torch.uint8,
+                      device=dev)
 
     def chunked():
         Lc.zero_()
         for (qc, kk, vv), qr, oo in zip(chunks, qb, oc):
             qr.copy_(qc)
             attn.kv_append(kk, vv, kc, vc, Lc, rope_theta=10000.0, q=qr)
-            attn.prefill_chunk(qr, kc, vc, Lc, scale, out=oo)
+            attn.prefill_chunk(qr, kc, vc, Lc, scale, out=oo, workspace=wsc)
     fo = torch.empty_like(q)
     mc = time_graph(chunked, 1, 5)
     mf = time_graph(lambda: attn.prefill_gqa_rope(q, k, v, scale, causal=True, rope_theta=10000.0, out=fo), 20, 5)

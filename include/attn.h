@@ -223,9 +223,10 @@ attn_status attn_combine_splits(const float* o_part, const float* lse_part, void
  * written (precondition: kv_len[b] + T <= cap).  Slots outside the appended
  * range are not touched.  k_new/v_new must not overlap the caches.
  * dtype: ATTN_F32, ATTN_F16 or ATTN_BF16; D even, at most 256, half rows a
- * whole number of 16-byte chunks; with RoPE cap <= 65536.  One kernel, one
- * workgroup per sequence, enqueued on `stream` (graph-capturable: the
- * lengths live on the device, so replays keep appending).
+ * whole number of 16-byte chunks; with RoPE cap <= 65536.  One kernel (a
+ * second, tiny one advances kv_len when a sequence's tokens are shared by
+ * several workgroups), enqueued on `stream` (graph-capturable: the lengths
+ * live on the device, so replays keep appending).
  *
  * attn_prefill_chunk attends a chunk of T query rows per sequence to the
  * cache prefix:
@@ -237,17 +238,26 @@ attn_status attn_combine_splits(const float* o_part, const float* lse_part, void
  * Row t of sequence b sits at position p = kv_len[b] - T + t and attends to
  * slots 0..p: O = softmax(scale q K^T) V with query head h reading KV head
  * h / (Hq/Hkv).  Rows with p < 0 have no key and get zeros (lse -inf).
+ * The key axis is cut into ranges of `split` keys (a multiple of 64; <= 0:
+ * a default from the shapes, aiming at ~512 workgroups) that run in
+ * parallel; when there is more than one range their partial results go to
+ * the caller's workspace (attn_prefill_chunk_workspace_bytes bytes,
+ * 256-byte aligned; 0 bytes, workspace may be NULL, when one range covers
+ * cap) and the combine kernel merges them.
  * dtype ATTN_BF16 or ATTN_F16 (others: ATTN_ERR_UNSUPPORTED); D 64 or 128;
- * T <= cap; scale a positive finite number.  One kernel on `stream`.
+ * T <= cap; scale a positive finite number; ATTN_ERR_WORKSPACE if the
+ * workspace is missing or too small.  One or two kernels on `stream`.
  * ------------------------------------------------------------------------ */
 attn_status attn_kv_append(const void* k_new, const void* v_new, void* q, void* k_cache,
                            void* v_cache, int32_t* kv_len, int B, int Hkv, int Hq, int T, int D,
                            int cap, attn_dtype dtype, float rope_theta, int advance,
                            hipStream_t stream);
+size_t attn_prefill_chunk_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int cap, int split);
 attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* kv_len, void* o, float* lse, int B, int Hq,
-                               int Hkv, int T, int D, int cap, attn_dtype dtype,
-                               attn_dtype out_dtype, float softmax_scale, hipStream_t stream);
+                               const int32_t* kv_len, void* o, float* lse, void* workspace,
+                               size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D,
+                               int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
+                               float softmax_scale, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -165,15 +165,30 @@ def test_kv_append_rejects(lib):
 
 
 def test_prefill_chunk_rejects(lib):
-    def chunk(q=P, kc=P, vc=P, L=P, o=P2, lse=None, B=2, Hq=16, Hkv=4, T=32, D=128, cap=2056,
-              dt=_lib.ATTN_BF16, odt=_lib.ATTN_BF16, scale=0.088):
-        return lib.attn_prefill_chunk(q, kc, vc, L, o, lse, B, Hq, Hkv, T, D, cap, dt, odt, scale, None)
+    def chunk(q=P, kc=P, vc=P, L=P, o=P2, lse=None, ws=P, wsb=None, B=2, Hq=16, Hkv=4, T=32, D=128, cap=2056,
+              split=0, dt=_lib.ATTN_BF16, odt=_lib.ATTN_BF16, scale=0.088):
+        if wsb is None:
+            wsb = lib.attn_prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split)
+        return lib.attn_prefill_chunk(q, kc, vc, L, o, lse, ws, wsb, B, Hq, Hkv, T, D, cap, split, dt, odt, scale,
+                                      None)
     assert chunk(L=None) == 1 and chunk(o=None) == 1
-    assert chunk(T=0) == 2 and chunk(T=3000) == 2 and chunk(Hq=6, Hkv=4) == 2
+    assert chunk(T=0) == 2 and chunk(T=3000) == 2 and chunk(Hq=6, Hkv=4) == 2 and chunk(split=100) == 2
     assert chunk(scale=0.0) == 2 and chunk(scale=float("nan")) == 2
     assert chunk(dt=_lib.ATTN_F32) == 6 and chunk(dt=_lib.ATTN_FP8_E5M2) == 6 and chunk(D=96) == 6
     assert chunk(odt=_lib.ATTN_FP8_E5M2) == 3 and chunk(dt=8) == 3
     assert chunk(q=ODD) == 4 and chunk(L=P + 2) == 4 and chunk(lse=P + 2) == 4
+    assert chunk(ws=None) == 5 and chunk(wsb=256) == 5 and chunk(ws=P + 16) == 4
+
+
+def test_prefill_chunk_workspace_size(lib):
+    # partials [B*Hq*T, nsplit, D] f32 then lse [B*Hq*T, nsplit] f32, 256-byte aligned pieces
+    B, Hq, Hkv, T, D, cap = 2, 16, 4, 32, 128, 2056
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    ns = -(-cap // 256)
+    assert lib.attn_prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, 256) == \
+        up(B * Hq * T * ns * D * 4) + up(B * Hq * T * ns * 4)
+    assert lib.attn_prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, 4096) == 0  # one range: none needed
+    assert lib.attn_prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, 0) > 0
 
 
 def test_binding_rejects_cpu_tensors():

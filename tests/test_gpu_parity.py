@@ -423,18 +423,22 @@ def test_kv_append_matches_oracle(attn, dtype, D, T, theta):
     assert np.all(np.abs(got_q - want_q) <= _REL[dtype] * np.maximum(np.abs(want_q), 1.0))
 
 
-@pytest.mark.parametrize("dtype,D,Hq,Hkv,T", [("bf16", 128, 16, 4, 32), ("bf16", 128, 16, 4, 1),
-                                              ("f16", 64, 8, 8, 45), ("bf16", 128, 8, 2, 32),
-                                              ("f16", 128, 4, 4, 130)])
-def test_prefill_chunk_matches_oracle(attn, dtype, D, Hq, Hkv, T):
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,T,split", [("bf16", 128, 16, 4, 32, 0), ("bf16", 128, 16, 4, 1, 0),
+                                                    ("f16", 64, 8, 8, 45, 64), ("bf16", 128, 8, 2, 32, 4096),
+                                                    ("f16", 128, 4, 4, 130, 192), ("bf16", 128, 16, 4, 32, 4096)])
+def test_prefill_chunk_matches_oracle(attn, dtype, D, Hq, Hkv, T, split):
     """Chunk rows at positions kv_len - T + t against the cache prefix, with
     ragged prefixes, NaN in every slot past kv_len (never read) and one
-    sequence shorter than the chunk (its leading rows see no key)."""
+    sequence shorter than the chunk (its leading rows see no key); key ranges
+    of the default size, of 64 and 192 keys (merged by the combine kernel,
+    with empty ranges) and one range for the whole cache (no workspace)."""
     B, cap = 4, 2056
     L = [T, 300 + T, cap, max(1, T // 2)]
     q = randn((B, Hq, T, D), dtype, 71, "q")
     _, kc, vc, kv_len = decode_gqa_inputs(B, Hq, Hkv, D, cap, 0, dtype, seed=72, nan_tail=True, lengths=L)
-    o, lse = attn.prefill_chunk(*_dev(q, kc, vc, kv_len), 1 / math.sqrt(D), return_lse=True)
+    if split == 4096:
+        assert attn.prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split) == 0
+    o, lse = attn.prefill_chunk(*_dev(q, kc, vc, kv_len), 1 / math.sqrt(D), return_lse=True, split=split)
     want, want_lse = oracle.prefill_chunk(to_f64(q), to_f64(kc), to_f64(vc), L, 1 / math.sqrt(D), return_lse=True)
     assert _maxerr(o, want) <= TOL[dtype]
     got_lse = to_f64(lse)
