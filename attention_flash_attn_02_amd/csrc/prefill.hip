@@ -59,6 +59,7 @@ struct PrefillParams {
   float rope_flo[64];
   float rope_fmid[64];  // three-way split (f_hi + f_mid + f_lo) for the fp32 kernel
   int halves;  // MFMA kernel: 1 = 4-wave workgroups, 2 = 8-wave split-key workgroups
+  int persist;  // 4-wave kernel with resident workgroups looping over items (grid < items)
   // chunked prefill against a cache prefix (prefill_fwd_kernel<..., CHUNK>)
   const int* kv_len;  // [B] key lengths including the chunk, device memory
   int cap;            // cache slots per head
@@ -457,9 +458,11 @@ __device__ inline float pair_sum32(float x) {
 // K/V rows come from caches with p.cap slots per head, the key length of
 // sequence b is kv_len[b] (read on the device) and query row r sits at
 // position kv_len[b] - p.S + r (causal with that offset).
-template <class Tag, int D, bool CAUSAL, bool ROPE, int HALVES, bool CHUNK = false>
+// PERSIST: resident workgroups loop over several items (see below).
+template <class Tag, int D, bool CAUSAL, bool ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false>
 __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const PrefillParams p) {
   static_assert(!CHUNK || (CAUSAL && !ROPE && HALVES == 1), "chunk mode: causal, no RoPE, 4 waves");
+  static_assert(!PERSIST || (HALVES == 1 && !CHUNK), "persistent scheduling: 4 waves, plain prefill");
   constexpr int BN = 64;
   constexpr int ROWB = D * 2;        // bytes per K/V row
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -519,7 +522,13 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
   int item_long = blockIdx.x, item_short = n_items - 1 - (int)blockIdx.x;
   if (HALVES == 1 && CAUSAL)
     item_long = (int)blockIdx.x < half_items ? (int)blockIdx.x : n_items - 1 - ((int)blockIdx.x - half_items);
-  const int n_my = (HALVES == 2 && CAUSAL && item_short > item_long) ? 2 : 1;
+  // persistent scheduling (4 waves): gridDim.x resident workgroups walk the
+  // longest-first item list in snake order, round k taking item
+  // k W + w (k even) or k W + W - 1 - w (k odd), so that every workgroup
+  // gets a balanced mix of long and short items
+  constexpr bool persist = PERSIST;
+  const int n_my = persist ? (n_items + (int)gridDim.x - 1) / (int)gridDim.x
+                           : (HALVES == 2 && CAUSAL && item_short > item_long) ? 2 : 1;
   // RoPE staging: row kr, chunk pairs (kj + 4u, + CH/2); 16 consecutive lanes
   // take 16 rows at one chunk so the LDS writes hit 16 distinct bank groups
   const int kr = (htid & 15) + 16 * (htid >> 6), kj = (htid >> 4) & 3;
@@ -546,7 +555,10 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
 #pragma unroll 1
   for (int itn = 0; itn < n_my; ++itn) {
     if (itn > 0) __syncthreads();  // LDS of the previous item is free
-    const int item_ks = itn == 0 ? item_long : item_short;
+    const int item_ks = persist ? itn * (int)gridDim.x + ((itn & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x
+                                                                    : (int)blockIdx.x)
+                                : itn == 0 ? item_long : item_short;
+    if (item_ks >= n_items) break;  // (persistent: uniform over the workgroup)
     const int split = CHUNK ? item_ks % p.nsplit : 0;  // key range of this item
     const int item = CHUNK ? item_ks / p.nsplit : item_ks;
     const int ptile = p.n_ptiles - 1 - item / per_ptile;
@@ -1408,7 +1420,24 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
 template <class Tag, int D, int H>
 static void launch_fwd_h(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
   const long long items = (long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups;
-  const dim3 grid((unsigned)(causal && H == 2 ? (items + 1) / 2 : items)), block(256 * H);
+  long long wgs = causal && H == 2 ? (items + 1) / 2 : items;
+  if (H == 1 && p.persist) {
+    // two resident workgroups per compute unit
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    wgs = std::min<long long>(items, 2LL * (cus > 0 ? cus : 256));
+  }
+  const dim3 grid((unsigned)wgs), block(256 * H);
+  if (H == 1 && p.persist) {
+    if (causal) {
+      if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, true, 1, false, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, false, 1, false, true>), grid, block, 0, st, p);
+    } else {
+      if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, true, 1, false, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, false, 1, false, true>), grid, block, 0, st, p);
+    }
+    return;
+  }
   if (causal) {
     if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, true, H>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, false, H>), grid, block, 0, st, p);
@@ -1439,7 +1468,7 @@ static void launch_pipe(const PrefillParams& p, bool causal, bool rope, hipStrea
 template <class Tag, int D>
 static void launch_16bit(const PrefillParams& p, int config, bool causal, bool rope, hipStream_t st) {
   if (config == 2) launch_pipe<Tag, D>(p, causal, rope, st);
-  else launch_fwd<Tag, D>(p, causal, rope, st);
+  else launch_fwd<Tag, D>(p, causal, rope, st);  // 0, 1, 3 (persistent 4-wave)
 }
 
 template <class Tag, int D, bool FP8>
@@ -1496,6 +1525,7 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   p.out_dtype = out_dtype;
   p.rope = rope ? 1 : 0;
   p.halves = config == 1 ? 2 : 1;
+  p.persist = config == 3 ? 1 : 0;
   if (rope && S > 65536) return ATTN_ERR_UNSUPPORTED;  // exact angle reduction needs pos < 2^16
   if (rope) {
     if (in_dtype == ATTN_F32) attn_host::rope_freq_split(rope_theta, D, p.inv_freq, p.rope_fhi, p.rope_flo, p.rope_fmid);
@@ -1541,8 +1571,11 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 //   0 (global default): 4-wave workgroups, 128 query rows, 64-key tiles;
 //   1: 8-wave workgroups whose two halves split the key tiles of 128 rows;
 //   2: the tiling of 0, software-pipelined (S of the next tile overlaps the
-//      softmax of this one).
-static const int kPrefillConfigs = 3;
+//      softmax of this one);
+//   3: the kernel of 0 with persistent scheduling: two resident workgroups per
+//      compute unit loop over the items (snake order over the longest-first
+//      list).
+static const int kPrefillConfigs = 4;
 
 extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, void* o,
                                              float* lse, int B, int Hq, int Hkv, int S, int D,

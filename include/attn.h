@@ -103,7 +103,11 @@ attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, v
  * configuration of each shape (the shape-adaptive attention lesson page,
  * row "Actual result": the global candidate's gap to the per-invocation
  * oracle).  For the 16-bit MFMA kernel: 0 = 4-wave workgroups of 128 query
- * rows; 1 = 8-wave workgroups whose halves split the key tiles of 128 rows.
+ * rows; 1 = 8-wave workgroups whose halves split the key tiles of 128 rows;
+ * 2 = the tiling of 0, software-pipelined (S of the next key tile issued
+ * during the softmax of this one); 3 = the kernel of 0 with persistent
+ * scheduling (two resident workgroups per compute unit loop over the items,
+ * snake order over the longest-first list).
  * fp32 and fp8 inputs ignore the id (one configuration).  An id out of range
  * returns ATTN_ERR_UNSUPPORTED. */
 int attn_prefill_num_configs(void);

@@ -83,14 +83,14 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S):
     assert _maxerr(lse, want_lse) <= 2e-2
 
 
-@pytest.mark.parametrize("config", [0, 1, 2])
+@pytest.mark.parametrize("config", [0, 1, 2, 3])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (4, 2)])
 @pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
                                                   (128, False, True, "f16"), (64, True, True, "bf16")])
 def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype):
     """Every tile configuration of the sweep passes parity before it is timed
     (GQA groups of 4, 1 and 2 query heads: different row layouts per wave)."""
-    assert attn.prefill_num_configs() == 3
+    assert attn.prefill_num_configs() == 4
     q, k, v = prefill_inputs(2, Hq, Hkv, 333, D, dtype, seed=config * 7 + D + Hq)
     theta = 10000.0 if rope else 0.0
     o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
@@ -116,6 +116,22 @@ def test_prefill_tile_counts(attn, S, D, causal, rope, Hq, Hkv):
                                     return_lse=True)
     assert _maxerr(o, want) <= TOL["bf16"]
     assert _maxerr(lse, want_lse) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,dtype,causal,theta", [(4, 32, 32, 4096, 128, "f16", True, 0.0),
+                                                            (2, 32, 8, 3000, 128, "bf16", True, 10000.0),
+                                                            (4, 16, 16, 2048, 64, "f16", False, 0.0)])
+def test_prefill_persistent_equals_default(attn, B, Hq, Hkv, S, D, dtype, causal, theta):
+    """Persistent scheduling (configuration 3) runs the per-item code of the
+    default configuration and only changes which workgroup takes which item:
+    at sizes where every resident workgroup loops over several items the two
+    outputs (and LSEs) are bit for bit equal."""
+    q, k, v = _dev(*prefill_inputs(B, Hq, Hkv, S, D, dtype, seed=S + D))
+    o0, l0 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta, config=0,
+                                   return_lse=True)
+    o3, l3 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta, config=3,
+                                   return_lse=True)
+    assert torch.equal(o0, o3) and torch.equal(l0, l3)
 
 
 def test_prefill_config_out_of_range(attn):
