@@ -104,6 +104,10 @@ __device__ inline uint32_t e5m2x2_to_f16x2(uint32_t two_bytes) {
 __device__ inline f32x16 mfma32_bf8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 1, 1, 0, 127, 0, 127);
 }
+// A in bf8 (e5m2), B in fp8 (e4m3), unit scales
+__device__ inline f32x16 mfma32_bf8_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 1, 0, 0, 127, 0, 127);
+}
 
 // ---------------------------------------------------------------------------
 // Small helpers

@@ -108,8 +108,10 @@ attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, v
  * during the softmax of this one); 3 = the kernel of 0 with persistent
  * scheduling (two resident workgroups per compute unit loop over the items,
  * snake order over the longest-first list).
- * fp32 and fp8 inputs ignore the id (one configuration).  An id out of range
- * returns ATTN_ERR_UNSUPPORTED. */
+ * fp8 inputs: 0 = P rounded to e4m3 for the PV MFMA (fp8 x bf8, twice the
+ * f16 rate), 1 = P in f16 with V upcast; other ids as 0.  fp32 inputs ignore
+ * the id (one configuration).  An id out of range returns
+ * ATTN_ERR_UNSUPPORTED. */
 int attn_prefill_num_configs(void);
 attn_status attn_prefill_gqa_rope_with_config(const void* q, const void* k, const void* v, void* o,
                                               float* lse, int B, int Hq, int Hkv, int S, int D,

@@ -185,15 +185,16 @@ def test_gqa_rope_full_size_sampled(attn):
     assert torch.isfinite(o.float()).all()
 
 
-@pytest.mark.parametrize("dtype", ["f16", "fp8_e5m2"])
+@pytest.mark.parametrize("dtype,config", [("f16", 0), ("fp8_e5m2", 0), ("fp8_e5m2", 1)])
 @pytest.mark.parametrize("D,causal", [(64, False), (128, True)])
 @pytest.mark.parametrize("N", [1024, 4096, 16384])
-def test_mha_forward_sampled(attn, dtype, D, causal, N):
+def test_mha_forward_sampled(attn, dtype, config, D, causal, N):
     """MHA forward Z=4, H=32 (fp16 or fp8 e5m2 in, fp16 out): sampled rows of
-    sampled heads, including (0, 0) and (3, 31)."""
+    sampled heads, including (0, 0) and (3, 31); fp8 with P in e4m3 on the
+    fp8 MFMA (configuration 0) and in f16 (configuration 1)."""
     q, k, v = prefill_inputs(4, 32, 32, N, D, dtype, seed=N + D)
     scale = 1 / math.sqrt(D)
-    o = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=causal, out_dtype=torch.float16).cpu()
+    o = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=causal, out_dtype=torch.float16, config=config).cpu()
     rng = np.random.default_rng(N)
     rows = sorted(set([0, 1, N // 2, N - 1] + list(rng.integers(0, N, 4))))
     heads = [(0, 0), (3, 31), (1, 7), (2, 20)]
@@ -212,6 +213,20 @@ def test_mha_forward_full_small(attn):
         o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.125, causal=False, out_dtype=torch.float16)
         want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 0.125, False)
         assert _maxerr(o, want) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("D,causal", [(64, False), (128, True)])
+def test_fp8_e4m3_p_full(attn, D, causal):
+    """fp8 inputs with P rounded to e4m3 for the PV MFMA (the fp8 default,
+    configuration 0): every element at N=1024 (with a ragged N=1000 too)
+    within the fp8 tolerance; the row sums are those of the rounded
+    probabilities."""
+    for N in (1024, 1000):
+        q, k, v = prefill_inputs(1, 8, 8, N, D, "fp8_e5m2", seed=N + D + 5)
+        o = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, out_dtype=torch.float16,
+                                  config=0)
+        want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal)
+        assert _maxerr(o, want) <= TOL["fp8_e5m2"]
 
 
 def test_prefill_descales(attn):
