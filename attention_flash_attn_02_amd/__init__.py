@@ -19,6 +19,7 @@ from .ops import (  # noqa: F401
     prefill_chunk_workspace_bytes,
     prefill_gqa_rope,
     prefill_gqa_rope_unfused,
+    prefill_gqa_rope_workspace_bytes,
     prefill_num_configs,
     rope_rotate,
 )

@@ -27,10 +27,14 @@ SIGNATURES = {
     "attn_prefill_gqa_rope": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_int, _c_float, _c_int, _c_float, _c_float, _c_float,
                                        _c_float, _vp]),
+    "attn_prefill_gqa_rope_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float]),
+    "attn_prefill_gqa_rope_ws": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_float, _c_int, _c_float, _c_float, _c_float,
+                                          _c_float, _vp, _sz, _vp]),
     "attn_prefill_num_configs": (_c_int, []),
     "attn_prefill_gqa_rope_with_config": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                                    _c_int, _c_int, _c_int, _c_float, _c_int, _c_float,
-                                                   _c_float, _c_float, _c_float, _c_int, _vp]),
+                                                   _c_float, _c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "attn_decode_gqa_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_decode_gqa": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _c_int, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _c_int, _c_float, _vp]),

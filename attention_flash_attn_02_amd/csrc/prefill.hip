@@ -512,7 +512,7 @@ __device__ inline float pair_sum32(float x) {
 // sequence b is kv_len[b] (read on the device) and query row r sits at
 // position kv_len[b] - p.S + r (causal with that offset).
 // PERSIST: resident workgroups loop over several items (see below).
-template <class Tag, int D, bool CAUSAL, bool ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false>
+template <class Tag, int D, bool CAUSAL, int ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false>
 __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const PrefillParams p) {
   static_assert(!CHUNK || (CAUSAL && !ROPE && HALVES == 1), "chunk mode: causal, no RoPE, 4 waves");
   static_assert(!PERSIST || (HALVES == 1 && !CHUNK), "persistent scheduling: 4 waves, plain prefill");
@@ -524,9 +524,12 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
   constexpr int IPW = BN / RPI / 4;  // direct loads per wave per tile
   constexpr int NKK = D / 16, NDB = D / 32, HALF = D / 2, PAIRS = D / 64;
   constexpr float kLazy = 8.f;
+  // RoPE mode: 0 none; 1 Q and K rotated here (K tiles while they are staged);
+  // 2 Q rotated here, K already rotated in HBM
+  constexpr bool RQ = ROPE != 0, RK = ROPE == 1;
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[HALVES * 4 * TILEB];  // [half][K0 K1 V0 V1]
-  __shared__ float rope_base[2][2][ROPE ? D : 1];                          // [half][slot][rev0 | freq]
+  __shared__ float rope_base[2][2][RK ? D : 1];                          // [half][slot][rev0 | freq]
 
   // XOR swizzles of the 16-byte chunks of a row, for a 64-bank LDS (one
   // 256-byte bank line = one D=128 row or two D=64 rows):
@@ -588,12 +591,12 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
   // frequency lane of the per-tile angle table, read from the kernel
   // arguments once (not inside the key loop, where the load latency would
   // hold up the filling wave every tile)
-  const float fhi_lane = ROPE && lane < HALF ? p.rope_fhi[lane] : 0.f;
-  const float flo_lane = ROPE && lane < HALF ? p.rope_flo[lane] : 0.f;
+  const float fhi_lane = RK && lane < HALF ? p.rope_fhi[lane] : 0.f;
+  const float flo_lane = RK && lane < HALF ? p.rope_flo[lane] : 0.f;
   // cos / sin of the row-offset angles kr f_j of this thread's K pairs
   // (kr < 64 and f_hi has 8 significant bits, so kr f_hi is exact)
-  float rcos[ROPE ? 8 * PAIRS : 1], rsin[ROPE ? 8 * PAIRS : 1];
-  if (ROPE) {
+  float rcos[RK ? 8 * PAIRS : 1], rsin[RK ? 8 * PAIRS : 1];
+  if (RK) {
 #pragma unroll
     for (int u = 0; u < PAIRS; ++u)
 #pragma unroll
@@ -646,7 +649,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
 #pragma unroll
         for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
       }
-      if (ROPE) {
+      if (RQ) {
 #pragma unroll
         for (int kk = 0; kk < NKK / 2; ++kk)
 #pragma unroll
@@ -692,7 +695,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
       for (int u = 0; u < IPW; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_AS(void, dst + RPI * (wq * IPW + u) * ROWB), 16, loff[u], 0, 0, 0);
     };
-    u32x4 kreg[ROPE ? 2 * PAIRS : 1];
+    u32x4 kreg[RK ? 2 * PAIRS : 1];
     auto load_k_regs = [&](int i) {
       const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, i);
 #pragma unroll
@@ -753,7 +756,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
     float l_run = 0.f;      // sum over this lane's keys of exp2(s - m_ref)
 
     // ---- prologue: local tile 0 into stage 0 ----
-    if (ROPE) {
+    if (RK) {
       rope_base_fill(0);
       rope_base_fill(1);
       if (exists(0)) {
@@ -774,10 +777,10 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
       const bool has_next = exists(i + 1);
       if (has_next) {
         dma(vg, vbuf(i + 1), dv, i + 1);
-        if (ROPE) load_k_regs(i + 1);
+        if (RK) load_k_regs(i + 1);
         else dma(kg, kbuf(i + 1), dk, i + 1);
       }
-      if (ROPE) rope_base_fill(i + 2);
+      if (RK) rope_base_fill(i + 2);
 
       if (active(i)) {
         // ---- S^T = K Q^T; A operands read from LDS three MFMAs ahead ----
@@ -878,7 +881,7 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
           }
         }
       }
-      if (ROPE && has_next) rotate_store_k(i + 1);
+      if (RK && has_next) rotate_store_k(i + 1);
     }
 
     // ---- merge the two halves (same rows, disjoint key tiles) ----
@@ -944,8 +947,11 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
 // unskewed kernel (ahead only at long sequences): it is a sweep
 // configuration, not the default.
 // ---------------------------------------------------------------------------
-template <class Tag, int D, bool CAUSAL, bool ROPE>
+template <class Tag, int D, bool CAUSAL, int ROPE>
 __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParams p) {
+  // RoPE mode: 0 none; 1 Q and K rotated here; 2 Q rotated here, K already
+  // rotated in HBM
+  constexpr bool RQ = ROPE != 0, RK = ROPE == 1;
   constexpr int BN = 64;
   constexpr int ROWB = D * 2;        // bytes per K/V row
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -956,7 +962,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
   constexpr float kLazy = 8.f;
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];  // [K0 K1 V0 V1]
-  __shared__ float rope_base[2][ROPE ? D : 1];                        // [slot][cos | sin]
+  __shared__ float rope_base[2][RK ? D : 1];                        // [slot][cos | sin]
 
   // chunk swizzles (see prefill_fwd_kernel)
   auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
@@ -998,10 +1004,10 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
   // RoPE on K: this thread rotates row kr (one of the rows its own wave
   // loaded) at chunk pairs (kj + 4u, + CH/2)
   const int kr = (lane & 15) + 16 * wq, kj = lane >> 4;
-  const float fhi_lane = ROPE && lane < HALF ? p.rope_fhi[lane] : 0.f;
-  const float flo_lane = ROPE && lane < HALF ? p.rope_flo[lane] : 0.f;
-  float rcos[ROPE ? 8 * PAIRS : 1], rsin[ROPE ? 8 * PAIRS : 1];
-  if (ROPE) {
+  const float fhi_lane = RK && lane < HALF ? p.rope_fhi[lane] : 0.f;
+  const float flo_lane = RK && lane < HALF ? p.rope_flo[lane] : 0.f;
+  float rcos[RK ? 8 * PAIRS : 1], rsin[RK ? 8 * PAIRS : 1];
+  if (RK) {
 #pragma unroll
     for (int u = 0; u < PAIRS; ++u)
 #pragma unroll
@@ -1036,7 +1042,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
 #pragma unroll
       for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
     }
-    if (ROPE) {
+    if (RQ) {
 #pragma unroll
       for (int kk = 0; kk < NKK / 2; ++kk)
 #pragma unroll
@@ -1271,7 +1277,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
     __builtin_amdgcn_s_waitcnt(0x3f70);  // this thread's loads have landed
     __syncthreads();                     // ... and everybody's; stages of tiles i-1 / i are free
     if (!decltype(last_two)::value) dma(kg, kbuf(i + 2), true, i + 2);
-    if (ROPE) rope_base_fill(i + 3);
+    if (RK) rope_base_fill(i + 3);
     {
       const int lim = mask_lim(i);
       const float m_use = softmax_head(decltype(last_two)::value ? row_max(cur, lim, last_two) : mx_pre);
@@ -1296,7 +1302,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
         __builtin_amdgcn_sched_group_barrier(0x402, 2, 1);
       }
     }
-    if (ROPE && !decltype(last_two)::value) {
+    if (RK && !decltype(last_two)::value) {
       __builtin_amdgcn_s_waitcnt(0x3f70);  // raw K(i+2) rows of this wave have landed
       rotate_k(i + 2);
     }
@@ -1310,7 +1316,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
 
   // ---- prologue: K(0), V(0), K(1) staged (and rotated), S(0) computed ----
   f32x16 s_a[2], s_b[2];
-  if (ROPE) {
+  if (RK) {
     rope_base_fill(0);
     rope_base_fill(1);
   }
@@ -1318,7 +1324,7 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
   dma(vg, vbuf(0), false, 0);
   if (exists(1)) dma(kg, kbuf(1), true, 1);
   __builtin_amdgcn_s_waitcnt(0x3f70);
-  if (ROPE) {
+  if (RK) {
     __syncthreads();  // base table visible
     rotate_k(0);
     if (exists(1)) rotate_k(1);
@@ -1470,56 +1476,59 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
 // ---------------------------------------------------------------------------
 // Host dispatch
 // ---------------------------------------------------------------------------
-template <class Tag, int D, int H>
-static void launch_fwd_h(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
+// rope: RoPE mode of the kernels (0 none, 1 Q and K rotated in the kernel,
+// 2 Q rotated in the kernel and K already rotated in HBM)
+template <class Tag, int D, int H, bool CAUSAL, int RM>
+static void launch_fwd_hr(const PrefillParams& p, hipStream_t st) {
   const long long items = (long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups;
-  long long wgs = causal && H == 2 ? (items + 1) / 2 : items;
+  long long wgs = CAUSAL && H == 2 ? (items + 1) / 2 : items;
   if (H == 1 && p.persist) {
     // two resident workgroups per compute unit
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
     wgs = std::min<long long>(items, 2LL * (cus > 0 ? cus : 256));
-  }
-  const dim3 grid((unsigned)wgs), block(256 * H);
-  if (H == 1 && p.persist) {
-    if (causal) {
-      if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, true, 1, false, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, false, 1, false, true>), grid, block, 0, st, p);
-    } else {
-      if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, true, 1, false, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, false, 1, false, true>), grid, block, 0, st, p);
-    }
+    hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, 1, false, true>), dim3((unsigned)wgs), dim3(256), 0, st, p);
     return;
   }
+  hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, H>), dim3((unsigned)wgs), dim3(256 * H), 0, st, p);
+}
+
+template <class Tag, int D, int H>
+static void launch_fwd_h(const PrefillParams& p, bool causal, int rope, hipStream_t st) {
   if (causal) {
-    if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, true, H>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, false, H>), grid, block, 0, st, p);
+    if (rope == 1) launch_fwd_hr<Tag, D, H, true, 1>(p, st);
+    else if (rope == 2) launch_fwd_hr<Tag, D, H, true, 2>(p, st);
+    else launch_fwd_hr<Tag, D, H, true, 0>(p, st);
   } else {
-    if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, true, H>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, false, H>), grid, block, 0, st, p);
+    if (rope == 1) launch_fwd_hr<Tag, D, H, false, 1>(p, st);
+    else if (rope == 2) launch_fwd_hr<Tag, D, H, false, 2>(p, st);
+    else launch_fwd_hr<Tag, D, H, false, 0>(p, st);
   }
 }
 
 template <class Tag, int D>
-static void launch_fwd(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
+static void launch_fwd(const PrefillParams& p, bool causal, int rope, hipStream_t st) {
   if (p.halves == 1) launch_fwd_h<Tag, D, 1>(p, causal, rope, st);
   else launch_fwd_h<Tag, D, 2>(p, causal, rope, st);
 }
 
 template <class Tag, int D>
-static void launch_pipe(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
+static void launch_pipe(const PrefillParams& p, bool causal, int rope, hipStream_t st) {
   const dim3 grid((unsigned)((long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups)), block(256);
   if (causal) {
-    if (rope) hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, true, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, true, false>), grid, block, 0, st, p);
+    if (rope == 1) hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, true, 1>), grid, block, 0, st, p);
+    else if (rope == 2) hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, true, 2>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, true, 0>), grid, block, 0, st, p);
   } else {
-    if (rope) hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, false, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, false, false>), grid, block, 0, st, p);
+    if (rope == 1) hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, false, 1>), grid, block, 0, st, p);
+    else if (rope == 2) hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, false, 2>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_pipe_kernel<Tag, D, false, 0>), grid, block, 0, st, p);
   }
 }
 
 template <class Tag, int D>
-static void launch_16bit(const PrefillParams& p, int config, bool causal, bool rope, hipStream_t st) {
+static void launch_16bit(const PrefillParams& p, int config, bool causal, int rope, hipStream_t st) {
   if (config == 2) launch_pipe<Tag, D>(p, causal, rope, st);
   else launch_fwd<Tag, D>(p, causal, rope, st);  // 0, 1, 3 (persistent 4-wave)
 }
@@ -1550,7 +1559,8 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
                                 int B, int Hq, int Hkv, int S, int D, attn_dtype in_dtype,
                                 attn_dtype out_dtype, float softmax_scale, int causal,
                                 float rope_theta, float q_descale, float k_descale,
-                                float v_descale, int config, hipStream_t stream) {
+                                float v_descale, int config, void* workspace,
+                                size_t workspace_bytes, bool use_ws, hipStream_t stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -1602,14 +1612,28 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   if (items > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   dim3 grid((unsigned)items);
   const bool c = causal != 0;
+  // RoPE on K with a workspace: every key is rotated once into the workspace
+  // (a K tile is shared by all query tiles of its KV head, so rotating it
+  // while staging repeats the work once per query tile); the attention
+  // kernel then rotates only its Q rows
+  int rope_mode = rope ? 1 : 0;
+  if (rope && use_ws && in_dtype != ATTN_FP8_E5M2) {
+    const size_t need = attn_prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, in_dtype, rope_theta);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!attn_host::aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+    const attn_status st = attn_rope_rotate(k, workspace, B, Hkv, S, D, in_dtype, rope_theta, stream);
+    if (st != ATTN_OK) return st;
+    p.k = workspace;
+    rope_mode = 2;
+  }
   switch (in_dtype) {
     case ATTN_BF16:
-      if (D == 64) launch_16bit<Bf16Tag, 64>(p, config, c, rope, stream);
-      else launch_16bit<Bf16Tag, 128>(p, config, c, rope, stream);
+      if (D == 64) launch_16bit<Bf16Tag, 64>(p, config, c, rope_mode, stream);
+      else launch_16bit<Bf16Tag, 128>(p, config, c, rope_mode, stream);
       break;
     case ATTN_F16:
-      if (D == 64) launch_16bit<F16Tag, 64>(p, config, c, rope, stream);
-      else launch_16bit<F16Tag, 128>(p, config, c, rope, stream);
+      if (D == 64) launch_16bit<F16Tag, 64>(p, config, c, rope_mode, stream);
+      else launch_16bit<F16Tag, 128>(p, config, c, rope_mode, stream);
       break;
     default:  // fp8 e5m2 (RoPE rejected above): P in e4m3 on the fp8 MFMA; configuration 1: P in f16
       if (config == 1) {
@@ -1635,6 +1659,13 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 //      list).
 static const int kPrefillConfigs = 4;
 
+extern "C" size_t attn_prefill_gqa_rope_workspace_bytes(int B, int Hkv, int S, int D, attn_dtype in_dtype,
+                                                       float rope_theta) {
+  if (B <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || !(rope_theta > 0.f)) return 0;
+  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return 0;  // fp32: own kernel; fp8: no RoPE
+  return (size_t)B * Hkv * S * D * 2;  // rotated K, same layout as k
+}
+
 extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, void* o,
                                              float* lse, int B, int Hq, int Hkv, int S, int D,
                                              attn_dtype in_dtype, attn_dtype out_dtype,
@@ -1642,17 +1673,28 @@ extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const
                                              float q_descale, float k_descale, float v_descale,
                                              hipStream_t stream) {
   return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, in_dtype, out_dtype, softmax_scale, causal,
-                      rope_theta, q_descale, k_descale, v_descale, 0, stream);
+                      rope_theta, q_descale, k_descale, v_descale, 0, nullptr, 0, false, stream);
+}
+
+extern "C" attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, const void* v, void* o,
+                                                float* lse, int B, int Hq, int Hkv, int S, int D,
+                                                attn_dtype in_dtype, attn_dtype out_dtype,
+                                                float softmax_scale, int causal, float rope_theta,
+                                                float q_descale, float k_descale, float v_descale,
+                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, in_dtype, out_dtype, softmax_scale, causal,
+                      rope_theta, q_descale, k_descale, v_descale, 0, workspace, workspace_bytes, true, stream);
 }
 
 extern "C" attn_status attn_prefill_gqa_rope_with_config(
     const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,
     int D, attn_dtype in_dtype, attn_dtype out_dtype, float softmax_scale, int causal,
     float rope_theta, float q_descale, float k_descale, float v_descale, int config,
-    hipStream_t stream) {
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (config < 0 || config >= kPrefillConfigs) return ATTN_ERR_UNSUPPORTED;
   return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, in_dtype, out_dtype, softmax_scale, causal,
-                      rope_theta, q_descale, k_descale, v_descale, config, stream);
+                      rope_theta, q_descale, k_descale, v_descale, config, workspace, workspace_bytes,
+                      workspace != nullptr, stream);
 }
 
 extern "C" int attn_prefill_num_configs(void) { return kPrefillConfigs; }

@@ -39,17 +39,29 @@ def prefill_num_configs() -> int:
     return int(_lib.lib().attn_prefill_num_configs())
 
 
+def prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, dtype, rope_theta) -> int:
+    return int(_lib.lib().attn_prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, _DT[dtype], float(rope_theta)))
+
+
 def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_theta: float = 0.0,
                      out_dtype=None, out=None, return_lse: bool = False, q_descale: float = 1.0,
-                     k_descale: float = 1.0, v_descale: float = 1.0, stream=None, config=None):
-    """attn_prefill_gqa_rope: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> o [B,Hq,S,D] (and lse [B,Hq,S]).
-    ``config`` selects a tile configuration (attn_prefill_gqa_rope_with_config); None = global."""
+                     k_descale: float = 1.0, v_descale: float = 1.0, stream=None, config=None,
+                     k_rope: str = "once", workspace=None):
+    """q [B,Hq,S,D], k/v [B,Hkv,S,D] -> o [B,Hq,S,D] (and lse [B,Hq,S]).
+
+    ``k_rope`` picks where RoPE is applied to K: "once" (attn_prefill_gqa_rope_ws:
+    every key rotated once into ``workspace``, allocated if not given, then the
+    attention kernel) or "per_tile" (attn_prefill_gqa_rope: K tiles rotated
+    inside the attention kernel as they are staged).  ``config`` selects a
+    tile configuration (attn_prefill_gqa_rope_with_config); None = global."""
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
         raise ValueError("k and v must be [B, Hkv, S, D] matching q")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
+    if k_rope not in ("once", "per_tile"):
+        raise ValueError("k_rope must be 'once' or 'per_tile'")
     if out_dtype is None:
         out_dtype = torch.float16 if q.dtype == torch.float8_e5m2 else q.dtype
     if out is None:
@@ -58,10 +70,20 @@ def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_th
     args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
             B, Hq, Hkv, S, D, _dtype_code(q), _dtype_code(out), float(softmax_scale), int(bool(causal)),
             float(rope_theta), float(q_descale), float(k_descale), float(v_descale)]
+    ws_ptr, ws_bytes = None, 0
+    if k_rope == "once":
+        need = int(_lib.lib().attn_prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, _dtype_code(q), float(rope_theta)))
+        if need > 0:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     if config is None:
-        code = _lib.lib().attn_prefill_gqa_rope(*args, _stream(stream))
+        if k_rope == "once":
+            code = _lib.lib().attn_prefill_gqa_rope_ws(*args, ws_ptr, ws_bytes, _stream(stream))
+        else:
+            code = _lib.lib().attn_prefill_gqa_rope(*args, _stream(stream))
     else:
-        code = _lib.lib().attn_prefill_gqa_rope_with_config(*args, int(config), _stream(stream))
+        code = _lib.lib().attn_prefill_gqa_rope_with_config(*args, int(config), ws_ptr, ws_bytes, _stream(stream))
     _lib.check(code)
     return (out, lse) if return_lse else out
 

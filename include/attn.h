@@ -88,6 +88,22 @@ const char* attn_status_str(attn_status s);
  * q_descale, k_descale multiply the scores and v_descale the output (per-
  * tensor dequantisation factors; pass 1.0 for unscaled inputs).
  * Math is fp32 with fp32 accumulation; 16-bit and fp8 inputs use MFMA.
+ *
+ * attn_prefill_gqa_rope rotates Q and K inside the attention kernel: each Q
+ * row once, each K tile while it is staged, i.e. once for every query tile
+ * that reads it.  One kernel on `stream`, no workspace.
+ *
+ * attn_prefill_gqa_rope_ws is the same operation with RoPE on K done once
+ * per key: a first kernel writes the rotated K to the caller's workspace
+ * (attn_prefill_gqa_rope_workspace_bytes() bytes, 16-byte aligned, not
+ * overlapping any other argument; contents on entry are ignored and on
+ * return hold the rotated K), then the attention kernel reads K from there
+ * and rotates only its Q rows.  Rotated values are rounded to in_dtype in
+ * both forms, so the two give the same result up to the angle's last
+ * bits.  The workspace size is B*Hkv*S*D*2 bytes for 16-bit inputs with
+ * rope_theta > 0 and 0 otherwise (then `workspace` may be NULL and only the
+ * attention kernel runs).  ATTN_ERR_WORKSPACE if it is needed and missing
+ * or too small.  Two kernels on `stream` (one without RoPE).
  * ------------------------------------------------------------------------ */
 attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, void* o,
                                   float* lse, int B, int Hq, int Hkv, int S, int D,
@@ -95,6 +111,14 @@ attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, v
                                   float softmax_scale, int causal, float rope_theta,
                                   float q_descale, float k_descale, float v_descale,
                                   hipStream_t stream);
+size_t attn_prefill_gqa_rope_workspace_bytes(int B, int Hkv, int S, int D, attn_dtype in_dtype,
+                                             float rope_theta);
+attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int B, int Hq, int Hkv, int S, int D,
+                                     attn_dtype in_dtype, attn_dtype out_dtype,
+                                     float softmax_scale, int causal, float rope_theta,
+                                     float q_descale, float k_descale, float v_descale,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Tile-configuration sweep: the same prefill with an explicit configuration
  * id in [0, attn_prefill_num_configs()).  Configuration 0 is the one global
@@ -111,14 +135,17 @@ attn_status attn_prefill_gqa_rope(const void* q, const void* k, const void* v, v
  * fp8 inputs: 0 = P rounded to e4m3 for the PV MFMA (fp8 x bf8, twice the
  * f16 rate), 1 = P in f16 with V upcast; other ids as 0.  fp32 inputs ignore
  * the id (one configuration).  An id out of range returns
- * ATTN_ERR_UNSUPPORTED. */
+ * ATTN_ERR_UNSUPPORTED.  With a NULL workspace K is rotated inside the
+ * kernel as in attn_prefill_gqa_rope; with a workspace, once per key first,
+ * as in attn_prefill_gqa_rope_ws. */
 int attn_prefill_num_configs(void);
 attn_status attn_prefill_gqa_rope_with_config(const void* q, const void* k, const void* v, void* o,
                                               float* lse, int B, int Hq, int Hkv, int S, int D,
                                               attn_dtype in_dtype, attn_dtype out_dtype,
                                               float softmax_scale, int causal, float rope_theta,
                                               float q_descale, float k_descale, float v_descale,
-                                              int config, hipStream_t stream);
+                                              int config, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Standalone RoPE rotation (the unfused form of the prefill's RoPE step; the

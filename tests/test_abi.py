@@ -71,6 +71,40 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, scale=float("nan")) == 2
 
 
+def _prefill_ws(lib, ws=P, ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P2, lse=None, B=1, Hq=4, Hkv=2, S=16, D=64, in_dt=_lib.ATTN_BF16,
+             out_dt=_lib.ATTN_BF16, scale=0.125, causal=1, theta=10000.0, qd=1.0, kd=1.0, vd=1.0)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.attn_prefill_gqa_rope_workspace_bytes(a["B"], a["Hkv"], a["S"], a["D"], a["in_dt"],
+                                                             a["theta"])
+    return lib.attn_prefill_gqa_rope_ws(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                        a["S"], a["D"], a["in_dt"], a["out_dt"], a["scale"], a["causal"],
+                                        a["theta"], a["qd"], a["kd"], a["vd"], ws, ws_bytes, None)
+
+
+def test_prefill_ws_workspace_size(lib):
+    f = lib.attn_prefill_gqa_rope_workspace_bytes
+    # rotated K: B * Hkv * S * D 16-bit elements
+    assert f(1, 8, 2048, 128, _lib.ATTN_BF16, 10000.0) == 1 * 8 * 2048 * 128 * 2
+    assert f(3, 2, 17, 64, _lib.ATTN_F16, 500.0) == 3 * 2 * 17 * 64 * 2
+    assert f(1, 8, 2048, 128, _lib.ATTN_BF16, 0.0) == 0  # no RoPE: no pre-pass
+    assert f(1, 8, 2048, 128, _lib.ATTN_F32, 10000.0) == 0  # fp32 kernel rotates K itself
+    assert f(1, 8, 2048, 128, _lib.ATTN_FP8_E5M2, 10000.0) == 0
+    assert f(0, 8, 2048, 128, _lib.ATTN_BF16, 10000.0) == 0
+
+
+def test_prefill_ws_rejects(lib):
+    assert _prefill_ws(lib, ws=None) == 5
+    assert _prefill_ws(lib, ws_bytes=16 * 64 * 2 * 2 - 1) == 5
+    assert _prefill_ws(lib, ws=P + 8) == 4
+    assert _prefill_ws(lib, q=None) == 1
+    assert _prefill_ws(lib, Hq=6, Hkv=4) == 2
+    assert _prefill_ws(lib, D=96) == 6
+    assert _prefill_ws(lib, S=70000) == 6  # exact angle reduction needs positions < 2^16
+    assert _prefill_ws(lib, in_dt=_lib.ATTN_FP8_E5M2, out_dt=_lib.ATTN_F16) == 6
+
+
 def _gqa(lib, ws_bytes=None, **kw):
     a = dict(q=P, k=P, v=P, L=P, o=P2, ws=P, B=2, Hq=16, Hkv=4, D=128, cap=300, split=128,
              dt=_lib.ATTN_BF16, scale=0.1)

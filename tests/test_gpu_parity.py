@@ -72,12 +72,15 @@ def test_tiny_f32_full(attn):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal,rope", [(True, True), (True, False), (False, True), (False, False)])
 @pytest.mark.parametrize("B,Hq,Hkv,S", [(2, 8, 2, 300), (1, 4, 4, 97), (1, 6, 3, 130)])
-def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S):
-    """Several tiles with a ragged tail, G = 4, 1 and 2; every output element checked."""
+@pytest.mark.parametrize("k_rope", ["once", "per_tile"])
+def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S, k_rope):
+    """Several tiles with a ragged tail, G = 4, 1 and 2; every output element
+    checked, with K rotated once into the workspace and per staged tile."""
     q, k, v = prefill_inputs(B, Hq, Hkv, S, D, dtype, seed=S + D)
     theta = 10000.0 if rope else 0.0
     scale = 1 / math.sqrt(D)
-    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=causal, rope_theta=theta, return_lse=True)
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=causal, rope_theta=theta, return_lse=True,
+                                   k_rope=k_rope)
     want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), scale, causal, theta, return_lse=True)
     assert _maxerr(o, want) <= TOL[dtype]
     assert _maxerr(lse, want_lse) <= 2e-2
@@ -87,14 +90,18 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S):
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (4, 2)])
 @pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
                                                   (128, False, True, "f16"), (64, True, True, "bf16")])
-def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype):
+@pytest.mark.parametrize("k_rope", ["once", "per_tile"])
+def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype, k_rope):
     """Every tile configuration of the sweep passes parity before it is timed
-    (GQA groups of 4, 1 and 2 query heads: different row layouts per wave)."""
+    (GQA groups of 4, 1 and 2 query heads: different row layouts per wave),
+    in both RoPE forms (K rotated once into the workspace, or per staged tile)."""
     assert attn.prefill_num_configs() == 4
+    if k_rope == "per_tile" and not rope:
+        pytest.skip("no RoPE: both forms are the same launch")
     q, k, v = prefill_inputs(2, Hq, Hkv, 333, D, dtype, seed=config * 7 + D + Hq)
     theta = 10000.0 if rope else 0.0
     o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
-                                   config=config, return_lse=True)
+                                   config=config, return_lse=True, k_rope=k_rope)
     want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta,
                                     return_lse=True)
     assert _maxerr(o, want) <= TOL[dtype]
@@ -132,6 +139,27 @@ def test_prefill_persistent_equals_default(attn, B, Hq, Hkv, S, D, dtype, causal
     o3, l3 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta, config=3,
                                    return_lse=True)
     assert torch.equal(o0, o3) and torch.equal(l0, l3)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,dtype", [(1, 32, 8, 2048, 128, "bf16"), (2, 8, 2, 1000, 64, "f16")])
+def test_prefill_k_rope_once_matches_per_tile(attn, B, Hq, Hkv, S, D, dtype):
+    """K rotated once into the workspace and K rotated per staged tile give
+    the same attention: both round the rotated K to the input type, and their
+    angles differ only in the last bits (the pre-pass reduces the angle with a
+    three-part frequency split, the staging path by angle addition), so a
+    rotated element may land on the neighbouring representable value.  The
+    workspace afterwards holds the rotated K, checked against the oracle's
+    rotation (within one rounding of the input type)."""
+    q, k, v = _dev(*prefill_inputs(B, Hq, Hkv, S, D, dtype, seed=S + 11))
+    ws = torch.empty(attn.prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, q.dtype, 10000.0), dtype=torch.uint8,
+                     device="cuda")
+    o1 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), rope_theta=10000.0, workspace=ws)
+    o2 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), rope_theta=10000.0, k_rope="per_tile")
+    assert float((o1.float() - o2.float()).abs().max()) <= 1e-2
+    krot = ws.view(q.dtype).view(B, Hkv, S, D)
+    want = oracle.rope_rotate(to_f64(k.cpu()), np.arange(S), 10000.0)
+    ulp = 2.0 ** (-7 if dtype == "bf16" else -10)
+    assert _maxerr(krot, want) <= ulp * float(np.max(np.abs(want)))
 
 
 def test_prefill_config_out_of_range(attn):
