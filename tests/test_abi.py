@@ -106,7 +106,7 @@ def test_prefill_ws_rejects(lib):
 
 
 def _gqa(lib, ws_bytes=None, **kw):
-    a = dict(q=P, k=P, v=P, L=P, o=P2, ws=P, B=2, Hq=16, Hkv=4, D=128, cap=300, split=128,
+    a = dict(q=P, k=P, v=P, L=P, o=P2, ws=P, B=2, Hq=16, Hkv=4, D=128, cap=3000, split=128,
              dt=_lib.ATTN_BF16, scale=0.1)
     a.update(kw)
     if ws_bytes is None:
@@ -125,22 +125,36 @@ def test_decode_gqa_rejects(lib):
     assert _gqa(lib, dt=11) == 3
     assert _gqa(lib, split=100) == 2
     assert _gqa(lib, split=2048) == 2
-    assert _gqa(lib, ws=None) == 5
+    assert _gqa(lib, ws=None) == 5                 # 6 workgroups per KV head: partials need a workspace
     assert _gqa(lib, ws_bytes=1024) == 5
     assert _gqa(lib, ws=P + 16) == 4
     assert _gqa(lib, o=ODD) == 4
 
 
 def test_decode_gqa_workspace_size(lib):
-    # partial outputs [B*Hq, nsplit, D] f32 then lse [B*Hq, nsplit] f32, 256-byte aligned pieces
+    # a KV head gets ceil(cap / (4 waves * split)) workgroups; with more than
+    # one, their partial outputs [B*Hq, n_wg, D] f32 then lse [B*Hq, n_wg] f32
+    # go to the workspace (256-byte aligned pieces); with one, none is needed
     B, Hq, cap, D, split = 128, 16, 2056, 128, 128
-    ns = -(-cap // split)
+    ns = -(-cap // (4 * split))
+    assert ns == 5
     o_bytes = B * Hq * ns * D * 4
     lse_bytes = B * Hq * ns * 4
     up = lambda x: -(-x // 256) * 256  # noqa: E731
     assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split) == up(o_bytes) + up(lse_bytes)
-    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 0) == lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 256)
+    # the default (1024 slots per wave) covers caps up to 4096 with one workgroup
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 0) == 0
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, 4096, D, 0) == 0
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, 4097, D, 0) == \
+        lib.attn_decode_gqa_workspace_bytes(B, Hq, 4097, D, 1024) > 0
     assert lib.attn_decode_gqa_workspace_bytes(0, Hq, cap, D, split) == 0
+
+
+def test_decode_gqa_no_workspace_when_one_workgroup(lib):
+    # cap 3000 at the default split: one workgroup per KV head, the workspace
+    # is not used, so NULL passes the host checks; a bad pointer elsewhere
+    # still fails them before anything is launched
+    assert _gqa(lib, split=0, ws=None, ws_bytes=0, o=ODD) == 4
 
 
 def _mla(lib, ws_bytes=None, **kw):
