@@ -8,11 +8,11 @@
 // all of them (the audit notes that such a row tile carries few useful query
 // rows; here they ride in the 16-wide N side of a 16x16x32 MFMA).
 //
-// Here the splits of a KV head are the waves of one workgroup, merged in LDS
-// at the end, so with the default (one workgroup per KV head) a decode step
-// is one kernel.  When several workgroups share a KV head, each writes its
-// part (o, lse) to the workspace and the combine kernel (combine.hip) merges
-// them.  Slots at or past kv_len are never loaded; a wave or workgroup
+// Here the splits of a KV head are the waves of a workgroup, merged in LDS
+// at the end.  When several workgroups share a KV head (the default), each
+// writes its part (o, lse) to the workspace and the combine kernel
+// (combine.hip) merges them; with one workgroup per KV head the result is
+// written directly and a decode step is one kernel.  Slots at or past kv_len are never loaded; a wave or workgroup
 // without slots contributes the empty part (o = 0, lse = -inf).
 
 #include "common.hpp"
@@ -272,9 +272,12 @@ static void launch_decode(const DecodeGqaParams& p, dim3 grid, hipStream_t st) {
 using namespace attn;
 
 // split: the most slots one wave streams.  A KV head gets
-// n_wg = ceil(cap / (waves * split)) workgroups; with the default one
-// workgroup covers a cache of up to 4096 slots, so no combine step runs.
-static const int kDefaultGqaSplit = 1024;
+// n_wg = ceil(cap / (waves * split)) workgroups.  The default, 128 (the
+// decode audit's split size), gives five workgroups per KV head at capacity
+// 2056: enough workgroups to fill the chip from batch 1, and a combine step
+// over five parts.  Splits of 1024 give one workgroup per KV head up to
+// capacity 4096 and no combine step (fastest only at large batch).
+static const int kDefaultGqaSplit = 128;
 
 static int gqa_split(int split) { return split <= 0 ? kDefaultGqaSplit : split; }
 

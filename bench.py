@@ -292,7 +292,7 @@ def sweep(scale):
     for kind, Bs, sc in (("gqa", (1, 8, 32, 64, 128), scale), ("mla", (1, 32, 128), 1 / math.sqrt(192))):
         for Bd in Bs:
             times = {}
-            for sp in (0, 64, 128, 256, 512):
+            for sp in (0, 64, 128, 256, 512, 1024):
                 r = decode_case(kind, Bd, sp, sc, modes=("cold",), iters=20)
                 times["default" if sp == 0 else str(sp)] = r["cold"]["graph_us"]
             best = min(times.values())

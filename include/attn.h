@@ -182,13 +182,18 @@ attn_status attn_rope_rotate(const void* x, void* y, int B, int H, int S, int D,
  *            never read, so they may hold anything, NaN included.
  *   o        [B, Hq, D]        dtype
  *   workspace: device scratch of at least attn_decode_gqa_workspace_bytes()
- *            bytes, 256-byte aligned; contents on entry are ignored.
+ *            bytes, 256-byte aligned; contents on entry are ignored.  When
+ *            that size is 0 the workspace is not used and may be NULL.
  *
- * The context is cut into splits of `split` slots aligned at slot 0
- * (split <= 0 picks the library default, 256); each split's partial
- * softmax is written to the workspace and merged by the combine step.
- * dtype: ATTN_BF16 or ATTN_F16.  D: 128.  Hq/Hkv <= 16.  split: a multiple
- * of 32 in [32, 1024].  Launches two kernels on `stream`.
+ * The context [0, kv_len[b]) of each KV head is cut into equal runs of
+ * 32-slot chunks, one per wave; `split` (<= 0: the library default, 128)
+ * is the most slots one wave streams.  The 4 waves of a workgroup merge
+ * their softmax parts in LDS; a KV head gets ceil(cap / (4 * split))
+ * workgroups, and when there is more than one their parts go to the
+ * workspace and a combine step merges them (with one, the output is
+ * written directly and a single kernel runs).  dtype: ATTN_BF16 or
+ * ATTN_F16.  D: 128.  Hq/Hkv <= 16.  split: a multiple of 32 in
+ * [32, 1024].  One or two kernels on `stream`.
  * ------------------------------------------------------------------------ */
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int cap, int D, int split);
 attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,

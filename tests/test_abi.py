@@ -142,19 +142,19 @@ def test_decode_gqa_workspace_size(lib):
     lse_bytes = B * Hq * ns * 4
     up = lambda x: -(-x // 256) * 256  # noqa: E731
     assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split) == up(o_bytes) + up(lse_bytes)
-    # the default (1024 slots per wave) covers caps up to 4096 with one workgroup
-    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 0) == 0
-    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, 4096, D, 0) == 0
-    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, 4097, D, 0) == \
-        lib.attn_decode_gqa_workspace_bytes(B, Hq, 4097, D, 1024) > 0
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 0) == lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 128)
+    # 1024 slots per wave cover caps up to 4096 with one workgroup: no workspace
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, cap, D, 1024) == 0
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, 4096, D, 1024) == 0
+    assert lib.attn_decode_gqa_workspace_bytes(B, Hq, 4097, D, 1024) > 0
     assert lib.attn_decode_gqa_workspace_bytes(0, Hq, cap, D, split) == 0
 
 
 def test_decode_gqa_no_workspace_when_one_workgroup(lib):
-    # cap 3000 at the default split: one workgroup per KV head, the workspace
-    # is not used, so NULL passes the host checks; a bad pointer elsewhere
-    # still fails them before anything is launched
-    assert _gqa(lib, split=0, ws=None, ws_bytes=0, o=ODD) == 4
+    # cap 3000 at split 1024: one workgroup per KV head, the workspace is not
+    # used, so NULL passes the host checks; a bad pointer elsewhere still
+    # fails them before anything is launched
+    assert _gqa(lib, split=1024, ws=None, ws_bytes=0, o=ODD) == 4
 
 
 def _mla(lib, ws_bytes=None, **kw):

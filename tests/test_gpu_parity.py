@@ -311,13 +311,14 @@ def test_prefill_unfused_matches_oracle(attn, D, Hq, Hkv, S):
 # ----------------------------------------------------------------------------
 # GQA decode
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("B,split", [(1, 128), (8, 128), (128, 128), (1, 0), (128, 0)])
+@pytest.mark.parametrize("B,split", [(1, 128), (8, 128), (128, 128), (1, 0), (128, 0), (8, 1024), (128, 1024)])
 def test_decode_gqa_config(attn, B, split):
     """GQA decode: Hq=16, Hkv=4, D=128, context 2048 in capacity 2056, at most
-    128 slots per wave (the decode audit's split size; five workgroups per KV
-    head merged by the combine kernel) and the library default (split=0, one
-    workgroup per KV head, the launch the benchmark times), bf16; slots
-    2048..2055 hold NaN and must never be read."""
+    128 slots per wave (the decode audit's split size and the library default
+    split=0, the launch the benchmark times: five workgroups per KV head
+    merged by the combine kernel) and 1024 (one workgroup per KV head that
+    writes the output itself), bf16; slots 2048..2055 hold NaN and must never
+    be read."""
     q, kc, vc, L = decode_gqa_inputs(B, 16, 4, 128, 2056, 2048, "bf16", nan_tail=True)
     scale = 1 / math.sqrt(128)
     o = attn.decode_gqa(*_dev(q, kc, vc, L), scale, split=split)
@@ -356,11 +357,11 @@ def test_decode_equals_prefill_row_on_gpu(attn):
         assert float((dec - full[:, :, t]).abs().max()) <= 2e-2
 
 
-@pytest.mark.parametrize("split", [128, 0])
+@pytest.mark.parametrize("split", [128, 1024])
 def test_decode_gqa_hipgraph_replay(attn, split):
     """Decode captured in a hipGraph replays to the eager result (lengths read
     from device); split 128 runs five workgroups per KV head and the combine
-    kernel, the default one workgroup that writes the output itself."""
+    kernel, split 1024 one workgroup that writes the output itself."""
     q, kc, vc, L = _dev(*decode_gqa_inputs(8, 16, 4, 128, 2056, 2048, "bf16", seed=2))
     ws = torch.empty(attn.decode_gqa_workspace_bytes(8, 16, 2056, 128, split), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
