@@ -1377,7 +1377,11 @@ __global__ __launch_bounds__(256, 2) void prefill_pipe_kernel(const PrefillParam
 }
 
 // ---------------------------------------------------------------------------
-// fp32 SIMT kernel: one query row per thread, 64 rows per workgroup.
+// fp32 SIMT kernel: L = 8 lanes per query row, 64 rows per workgroup.  Lane
+// g of a row holds the rotate-half pairs (i, i + D/2) for i in
+// [g D/(2L), (g+1) D/(2L)), so RoPE on Q stays inside the lane; the partial
+// dot products of the L lanes are summed with xor shuffles and every lane
+// runs the same online softmax over its share of the output.
 // ---------------------------------------------------------------------------
 // cos / sin of angle pos * w_i for the fp32 kernel: the angle is reduced to
 // one revolution exactly (three-part frequency split) before the radian
@@ -1389,29 +1393,41 @@ __device__ inline void rope_sincos_exact(const PrefillParams& p, int pos, int i,
   sincosf(6.283185307179586f * rev, sn, cs);
 }
 
+constexpr int kF32Lanes = 8;  // lanes per query row of the fp32 kernel
+
 template <int D, bool CAUSAL, bool ROPE>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(64 * kF32Lanes) void prefill_f32_kernel(const PrefillParams p) {
   constexpr int BN = 32;
   constexpr int HALF = D / 2;
+  constexpr int LPR = kF32Lanes;    // lanes per query row
+  constexpr int NT = 64 * LPR;      // threads per workgroup (64 rows)
+  constexpr int QP = HALF / LPR;    // rotate-half pairs per lane
   __shared__ float ks[BN][D];
   __shared__ float vs[BN][D];
   const int tid = threadIdx.x;
+  const int g = tid & (LPR - 1), rl = tid / LPR;  // lane of the row, row of the workgroup
   const int head = blockIdx.y, b = blockIdx.z;
   const int kvh = head / p.G;
   const int r0 = blockIdx.x * 64;
-  const int qpos = r0 + tid;
+  const int qpos = r0 + rl;
+  const int i0 = g * QP;  // this lane's pairs: dims i0 .. i0+QP-1 and HALF+i0 ..
   const float* qsrc = reinterpret_cast<const float*>(p.q) + (((size_t)b * p.Hq + head) * p.S + min(qpos, p.S - 1)) * D;
-  float q[D], o[D];
+  float q[2 * QP], o[2 * QP];
 #pragma unroll
-  for (int d = 0; d < D; ++d) { q[d] = qsrc[d]; o[d] = 0.f; }
+  for (int i = 0; i < QP; ++i) {
+    q[i] = qsrc[i0 + i];
+    q[QP + i] = qsrc[HALF + i0 + i];
+    o[i] = 0.f;
+    o[QP + i] = 0.f;
+  }
   if (ROPE) {
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) {
+    for (int i = 0; i < QP; ++i) {
       float sn, cs;
-      rope_sincos_exact(p, qpos, i, &sn, &cs);
-      const float x1 = q[i], x2 = q[i + HALF];
+      rope_sincos_exact(p, qpos, i0 + i, &sn, &cs);
+      const float x1 = q[i], x2 = q[QP + i];
       q[i] = x1 * cs - x2 * sn;
-      q[i + HALF] = x2 * cs + x1 * sn;
+      q[QP + i] = x2 * cs + x1 * sn;
     }
   }
   const int kend = CAUSAL ? min(p.S, r0 + 64) : p.S;
@@ -1420,7 +1436,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
   float m_run = kNegInf, l_run = 0.f;
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();
-    for (int e = tid; e < BN * D; e += 64) {
+    for (int e = tid; e < BN * D; e += NT) {
       const int r = e / D, d = e % D;
       const int key = k0 + r;
       ks[r][d] = key < p.S ? kbase[(size_t)key * D + d] : 0.f;
@@ -1428,7 +1444,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
     }
     if (ROPE) {
       __syncthreads();
-      for (int e = tid; e < BN * HALF; e += 64) {
+      for (int e = tid; e < BN * HALF; e += NT) {
         const int r = e / HALF, i = e % HALF;
         float sn, cs;
         rope_sincos_exact(p, k0 + r, i, &sn, &cs);
@@ -1444,7 +1460,12 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
     for (int j = 0; j < BN; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc = fmaf(q[d], ks[j][d], acc);
+      for (int i = 0; i < QP; ++i) {
+        acc = fmaf(q[i], ks[j][i0 + i], acc);
+        acc = fmaf(q[QP + i], ks[j][HALF + i0 + i], acc);
+      }
+#pragma unroll
+      for (int x = 1; x < LPR; x <<= 1) acc += __shfl_xor(acc, x);
       const int key = k0 + j;
       s[j] = (key >= p.S || (CAUSAL && key > qpos)) ? kNegInf : acc * p.scale_log2;
       mx = fmaxf(mx, s[j]);
@@ -1455,21 +1476,28 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillParams p) 
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] *= alpha;
+    for (int i = 0; i < 2 * QP; ++i) o[i] *= alpha;
 #pragma unroll
     for (int j = 0; j < BN; ++j) {
       const float pj = exp2f(s[j] - m_use);
       l_run += pj;
 #pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = fmaf(pj, vs[j][d], o[d]);
+      for (int i = 0; i < QP; ++i) {
+        o[i] = fmaf(pj, vs[j][i0 + i], o[i]);
+        o[QP + i] = fmaf(pj, vs[j][HALF + i0 + i], o[QP + i]);
+      }
     }
   }
   if (qpos < p.S) {
     const float inv = l_run > 0.f ? p.out_scale / l_run : 0.f;
     const size_t obase = (((size_t)b * p.Hq + head) * p.S + qpos) * D;
 #pragma unroll
-    for (int d = 0; d < D; d += 4) store4(p.o, obase + d, p.out_dtype, o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
-    if (p.lse) p.lse[((size_t)b * p.Hq + head) * p.S + qpos] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
+    for (int i = 0; i < QP; i += 4) {
+      store4(p.o, obase + i0 + i, p.out_dtype, o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
+      store4(p.o, obase + HALF + i0 + i, p.out_dtype, o[QP + i] * inv, o[QP + i + 1] * inv, o[QP + i + 2] * inv,
+             o[QP + i + 3] * inv);
+    }
+    if (p.lse && g == 0) p.lse[((size_t)b * p.Hq + head) * p.S + qpos] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
   }
 }
 
@@ -1541,13 +1569,13 @@ static void launch_mfma(const PrefillParams& p, bool causal, dim3 grid, hipStrea
 
 template <int D>
 static void launch_f32(const PrefillParams& p, bool causal, bool rope, hipStream_t st) {
-  dim3 grid((p.S + 63) / 64, p.Hq, p.B);
+  dim3 grid((p.S + 63) / 64, p.Hq, p.B), block(64 * kF32Lanes);  // 64 rows x kF32Lanes lanes
   if (causal) {
-    if (rope) hipLaunchKernelGGL((prefill_f32_kernel<D, true, true>), grid, dim3(64), 0, st, p);
-    else hipLaunchKernelGGL((prefill_f32_kernel<D, true, false>), grid, dim3(64), 0, st, p);
+    if (rope) hipLaunchKernelGGL((prefill_f32_kernel<D, true, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_f32_kernel<D, true, false>), grid, block, 0, st, p);
   } else {
-    if (rope) hipLaunchKernelGGL((prefill_f32_kernel<D, false, true>), grid, dim3(64), 0, st, p);
-    else hipLaunchKernelGGL((prefill_f32_kernel<D, false, false>), grid, dim3(64), 0, st, p);
+    if (rope) hipLaunchKernelGGL((prefill_f32_kernel<D, false, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_f32_kernel<D, false, false>), grid, block, 0, st, p);
   }
 }
 

@@ -59,6 +59,20 @@ def test_prefill_f32_rope(attn, S, rows):
             assert _maxerr(o[0, h, rows], want) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("D,causal,rope", [(128, True, True), (128, False, False), (64, False, True),
+                                           (128, True, False)])
+def test_prefill_f32_full(attn, D, causal, rope):
+    """fp32 prefill (SIMT kernel, eight lanes per row): every element and the
+    log-sum-exp at the fp32 tolerance, GQA G=2, a ragged last row block."""
+    q, k, v = prefill_inputs(2, 4, 2, 200, D, "f32", seed=D + 3)
+    theta = 10000.0 if rope else 0.0
+    scale = 1 / math.sqrt(D)
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=causal, rope_theta=theta, return_lse=True)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), scale, causal, theta, return_lse=True)
+    assert _maxerr(o, want) <= TOL["f32"]
+    assert _maxerr(lse, want_lse) <= 1e-5
+
+
 def test_tiny_f32_full(attn):
     """Tiny causal GQA prefill, fp32: B=1, Hq=4, Hkv=2, S=128, D=64, scale 1/8."""
     q, k, v = prefill_inputs(1, 4, 2, 128, 64, "f32")
