@@ -1511,13 +1511,18 @@ static void launch_fwd_hr(const PrefillParams& p, hipStream_t st) {
   const long long items = (long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups;
   long long wgs = CAUSAL && H == 2 ? (items + 1) / 2 : items;
   if (H == 1 && p.persist) {
-    // two resident workgroups per compute unit
+    // two resident workgroups per compute unit loop over the items once
+    // there are more than two rounds of them; up to two rounds the hardware
+    // dispatcher's refill (one workgroup per item) is as good or better
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    wgs = std::min<long long>(items, 2LL * (cus > 0 ? cus : 256));
-    hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, 1, false, true>), dim3((unsigned)wgs), dim3(256), 0, st, p);
-    return;
+    const long long resident = 2LL * (cus > 0 ? cus : 256);
+    if (items > 2 * resident) {
+      hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, 1, false, true>), dim3((unsigned)resident), dim3(256), 0,
+                         st, p);
+      return;
+    }
   }
   hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, H>), dim3((unsigned)wgs), dim3(256 * H), 0, st, p);
 }
@@ -1676,16 +1681,20 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   return attn_host::launch_status();
 }
 
-// Tile configurations of the 16-bit MFMA prefill kernel (fp32 and fp8 inputs
-// have a single configuration):
-//   0 (global default): 4-wave workgroups, 128 query rows, 64-key tiles;
+// Tile configurations of the 16-bit MFMA prefill kernel (fp32 inputs have a
+// single configuration; fp8 inputs use 1 for P in f16 and the default
+// otherwise):
+//   0 (global default): 4-wave workgroups, 128 query rows, 64-key tiles, one
+//      workgroup per work item;
 //   1: 8-wave workgroups whose two halves split the key tiles of 128 rows;
 //   2: the tiling of 0, software-pipelined (S of the next tile overlaps the
 //      softmax of this one);
-//   3: the kernel of 0 with persistent scheduling: two resident workgroups per
-//      compute unit loop over the items (snake order over the longest-first
-//      list).
+//   3: the kernel of 0 with persistent scheduling once the work exceeds two
+//      residency rounds: two resident workgroups per compute unit loop over
+//      the items (snake order over the longest-first list); up to two rounds
+//      it launches as 0.
 static const int kPrefillConfigs = 4;
+static const int kPrefillGlobalConfig = 0;
 
 extern "C" size_t attn_prefill_gqa_rope_workspace_bytes(int B, int Hkv, int S, int D, attn_dtype in_dtype,
                                                        float rope_theta) {
@@ -1701,7 +1710,7 @@ extern "C" attn_status attn_prefill_gqa_rope(const void* q, const void* k, const
                                              float q_descale, float k_descale, float v_descale,
                                              hipStream_t stream) {
   return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, in_dtype, out_dtype, softmax_scale, causal,
-                      rope_theta, q_descale, k_descale, v_descale, 0, nullptr, 0, false, stream);
+                      rope_theta, q_descale, k_descale, v_descale, kPrefillGlobalConfig, nullptr, 0, false, stream);
 }
 
 extern "C" attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, const void* v, void* o,
@@ -1711,7 +1720,8 @@ extern "C" attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, co
                                                 float q_descale, float k_descale, float v_descale,
                                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, in_dtype, out_dtype, softmax_scale, causal,
-                      rope_theta, q_descale, k_descale, v_descale, 0, workspace, workspace_bytes, true, stream);
+                      rope_theta, q_descale, k_descale, v_descale, kPrefillGlobalConfig, workspace, workspace_bytes,
+                      true, stream);
 }
 
 extern "C" attn_status attn_prefill_gqa_rope_with_config(

@@ -17,6 +17,7 @@ import argparse
 import json
 import math
 import os
+import random
 import sys
 import time
 
@@ -46,11 +47,30 @@ def mla_decode_bytes(B, H=16, dq=512, dl=448, L=2048, elem=2):
     return B * (L * dq * elem + H * dq * elem + H * dl * elem)
 
 
+SPIN_S = 0.06  # untimed work before each measurement: the clock takes ~45 ms of load to settle
+
+
+def spin(fn, seconds=SPIN_S):
+    """Run fn() back to back for about `seconds` of wall time (untimed), so that
+    the measurement that follows sees the clock it settles at under load."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                break
+
+
 def time_loop(fn, iters, warmup):
     """Average ms per call of fn() over `iters` calls, HIP events on the current stream."""
     import torch
     for _ in range(warmup):
         fn()
+    spin(fn)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
@@ -77,6 +97,7 @@ def time_graph(fn, steps_per_graph, replays, warmup=2):
     torch.cuda.synchronize()
     for _ in range(warmup):
         g.replay()
+    spin(g.replay)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
@@ -258,10 +279,15 @@ def decode_neighbours(iters=50):
     return out
 
 
+SWEEP_ROUNDS = 3
+
+
 def sweep(scale):
     """Every tile configuration per shape; gap of the global configuration to the best one.
 
-    Prefill: attn_prefill_gqa_rope_with_config ids (global = 0).  Decode: the
+    Prefill: attn_prefill_gqa_rope_with_config ids (global = 0), timed in
+    SWEEP_ROUNDS interleaved rounds (seeded random order), median per
+    configuration.  Decode: the
     split size (global = the library default), hipGraph mode, cold caches."""
     import torch
     import attention_flash_attn_02_amd as attn
@@ -280,11 +306,18 @@ def sweep(scale):
         ws = torch.empty(max(1, attn.prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, q.dtype, theta)),
                          dtype=torch.uint8, device=dev)
         it = 20 if S <= 4096 else 4
-        times = {}
-        for c in range(nconf):
-            ms = time_loop(lambda: attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta,
-                                                        out=o, config=c, workspace=ws), it, 2)
-            times[str(c)] = round(ms * 1e3, 2)
+        # configurations interleaved over rounds in a seeded random order, median per configuration
+        rng = random.Random(S * 7 + D)
+        samples = {c: [] for c in range(nconf)}
+        for rnd in range(SWEEP_ROUNDS):
+            order = list(range(nconf))
+            rng.shuffle(order)
+            for c in order:
+                ms = time_loop(lambda: attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal,
+                                                            rope_theta=theta, out=o, config=c, workspace=ws),
+                               it, 2)
+                samples[c].append(ms)
+        times = {str(c): round(sorted(v)[len(v) // 2] * 1e3, 2) for c, v in samples.items()}
         best = min(times.values())
         out["prefill_" + name] = {"us": times, "global": "0", "best": min(times, key=times.get),
                                   "gap_pct": round(100 * (times["0"] / best - 1), 2)}
@@ -365,7 +398,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps before the timed ones (the clock settles after ~800 steps)")
     ap.add_argument("--quick", action="store_true", help="prefill step only (for profiling runs)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only GQA and MLA decode at batch 128 with the default splits, `steps` calls "

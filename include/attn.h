@@ -122,22 +122,24 @@ attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, const void* v
 
 /* Tile-configuration sweep: the same prefill with an explicit configuration
  * id in [0, attn_prefill_num_configs()).  Configuration 0 is the one global
- * configuration attn_prefill_gqa_rope uses; the others exist so that a
- * per-shape sweep can measure how far the global choice is from the best
- * configuration of each shape (the shape-adaptive attention lesson page,
- * row "Actual result": the global candidate's gap to the per-invocation
- * oracle).  For the 16-bit MFMA kernel: 0 = 4-wave workgroups of 128 query
- * rows; 1 = 8-wave workgroups whose halves split the key tiles of 128 rows;
- * 2 = the tiling of 0, software-pipelined (S of the next key tile issued
- * during the softmax of this one); 3 = the kernel of 0 with persistent
- * scheduling (two resident workgroups per compute unit loop over the items,
- * snake order over the longest-first list).
- * fp8 inputs: 0 = P rounded to e4m3 for the PV MFMA (fp8 x bf8, twice the
- * f16 rate), 1 = P in f16 with V upcast; other ids as 0.  fp32 inputs ignore
- * the id (one configuration).  An id out of range returns
- * ATTN_ERR_UNSUPPORTED.  With a NULL workspace K is rotated inside the
- * kernel as in attn_prefill_gqa_rope; with a workspace, once per key first,
- * as in attn_prefill_gqa_rope_ws. */
+ * configuration attn_prefill_gqa_rope and attn_prefill_gqa_rope_ws use; the
+ * others exist so that a per-shape sweep can measure how far the global
+ * choice is from the best configuration of each shape (the shape-adaptive
+ * attention lesson page, row "Actual result": the global candidate's gap to
+ * the per-invocation oracle).  For the 16-bit MFMA kernel: 0 = 4-wave
+ * workgroups of 128 query rows, one workgroup per work item; 1 = 8-wave
+ * workgroups whose halves split the key tiles of 128 rows; 2 = the tiling
+ * of 0, software-pipelined (S of the next key tile issued during the softmax
+ * of this one); 3 = the kernel of 0 with persistent scheduling when the work
+ * items exceed two residency rounds (two resident workgroups per compute
+ * unit loop over the items, snake order over the longest-first list), and
+ * launched as 0 otherwise.
+ * fp8 inputs: 1 = P in f16 with V upcast; every other id = P rounded to e4m3
+ * for the PV MFMA (fp8 x bf8, twice the f16 rate).  fp32 inputs ignore the
+ * id (one configuration).  An id out of range returns ATTN_ERR_UNSUPPORTED.
+ * With a NULL workspace K is rotated inside the kernel as in
+ * attn_prefill_gqa_rope; with a workspace, once per key first, as in
+ * attn_prefill_gqa_rope_ws. */
 int attn_prefill_num_configs(void);
 attn_status attn_prefill_gqa_rope_with_config(const void* q, const void* k, const void* v, void* o,
                                               float* lse, int B, int Hq, int Hkv, int S, int D,
