@@ -439,12 +439,23 @@ def test_decode_mla_fewer_heads_f16(attn):
 # ----------------------------------------------------------------------------
 # Combine on its own
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("D,ns,empty", [(128, 17, 0), (448, 9, 3), (64, 5, 1), (1000, 3, 2)])
+@pytest.mark.parametrize("D,ns,empty", [(128, 17, 0), (448, 9, 3), (64, 5, 1), (1000, 3, 2), (128, 1, 0),
+                                        (128, 8, 2), (64, 16, 5), (448, 16, 0), (128, 24, 4)])
 def test_combine_matches_pairwise_merge(attn, D, ns, empty):
+    """The combine kernels (all parts loaded up front for up to 8 parts, a loop
+    beyond) against the oracle's merge, with empty parts."""
     o_part, lse = split_partials(40, ns, D, seed=D, empty_every=empty)
     got = attn.combine_splits(*_dev(o_part, lse))
     want = oracle.combine_splits(o_part.numpy(), lse.numpy())
     assert _maxerr(got, want) <= 1e-5
+
+
+@pytest.mark.parametrize("ns", [3, 12, 20])
+def test_combine_all_parts_empty(attn, ns):
+    """A row whose parts are all empty (lse -inf) is written as zeros."""
+    o_part, lse = split_partials(8, ns, 128, seed=ns, empty_every=1)
+    got = attn.combine_splits(*_dev(o_part, lse)).cpu()
+    assert torch.all(got == 0)
 
 
 # ----------------------------------------------------------------------------
