@@ -18,6 +18,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_
                 4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_UNSUPPORTED",
                 7: "ATTN_ERR_LAUNCH"}
 ATTN_F32, ATTN_F16, ATTN_BF16, ATTN_FP8_E5M2 = 0, 1, 2, 3
+ATTN_CONFIG_K_ROTATED = 0x100  # or-ed into a prefill configuration id: the workspace holds the rotated K
 
 _c_int, _c_float, _vp, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 

@@ -1593,7 +1593,8 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
                                 attn_dtype out_dtype, float softmax_scale, int causal,
                                 float rope_theta, float q_descale, float k_descale,
                                 float v_descale, int config, void* workspace,
-                                size_t workspace_bytes, bool use_ws, hipStream_t stream) {
+                                size_t workspace_bytes, bool use_ws, hipStream_t stream,
+                                bool k_rotated = false) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -1649,13 +1650,16 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   // (a K tile is shared by all query tiles of its KV head, so rotating it
   // while staging repeats the work once per query tile); the attention
   // kernel then rotates only its Q rows
+  // (k_rotated: the workspace already holds this K rotated; the pre-pass is skipped)
   int rope_mode = rope ? 1 : 0;
   if (rope && use_ws && in_dtype != ATTN_FP8_E5M2) {
     const size_t need = attn_prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, in_dtype, rope_theta);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!attn_host::aligned(workspace, 16)) return ATTN_ERR_ALIGN;
-    const attn_status st = attn_rope_rotate(k, workspace, B, Hkv, S, D, in_dtype, rope_theta, stream);
-    if (st != ATTN_OK) return st;
+    if (!k_rotated) {
+      const attn_status st = attn_rope_rotate(k, workspace, B, Hkv, S, D, in_dtype, rope_theta, stream);
+      if (st != ATTN_OK) return st;
+    }
     p.k = workspace;
     rope_mode = 2;
   }
@@ -1729,10 +1733,13 @@ extern "C" attn_status attn_prefill_gqa_rope_with_config(
     int D, attn_dtype in_dtype, attn_dtype out_dtype, float softmax_scale, int causal,
     float rope_theta, float q_descale, float k_descale, float v_descale, int config,
     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const bool k_rotated = (config & ATTN_CONFIG_K_ROTATED) != 0;
+  config &= ~ATTN_CONFIG_K_ROTATED;
   if (config < 0 || config >= kPrefillConfigs) return ATTN_ERR_UNSUPPORTED;
+  if (k_rotated && !workspace) return ATTN_ERR_WORKSPACE;
   return prefill_impl(q, k, v, o, lse, B, Hq, Hkv, S, D, in_dtype, out_dtype, softmax_scale, causal,
                       rope_theta, q_descale, k_descale, v_descale, config, workspace, workspace_bytes,
-                      workspace != nullptr, stream);
+                      workspace != nullptr, stream, k_rotated);
 }
 
 extern "C" int attn_prefill_num_configs(void) { return kPrefillConfigs; }

@@ -46,14 +46,16 @@ def prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, dtype, rope_theta) -> int:
 def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_theta: float = 0.0,
                      out_dtype=None, out=None, return_lse: bool = False, q_descale: float = 1.0,
                      k_descale: float = 1.0, v_descale: float = 1.0, stream=None, config=None,
-                     k_rope: str = "once", workspace=None):
+                     k_rope: str = "once", workspace=None, k_rotated: bool = False):
     """q [B,Hq,S,D], k/v [B,Hkv,S,D] -> o [B,Hq,S,D] (and lse [B,Hq,S]).
 
     ``k_rope`` picks where RoPE is applied to K: "once" (attn_prefill_gqa_rope_ws:
     every key rotated once into ``workspace``, allocated if not given, then the
     attention kernel) or "per_tile" (attn_prefill_gqa_rope: K tiles rotated
     inside the attention kernel as they are staged).  ``config`` selects a
-    tile configuration (attn_prefill_gqa_rope_with_config); None = global."""
+    tile configuration (attn_prefill_gqa_rope_with_config); None = global.
+    ``k_rotated`` (with a configuration and a workspace): the workspace already
+    holds this K rotated by an earlier call, so only the attention kernel runs."""
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
@@ -62,6 +64,8 @@ def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_th
         raise TypeError("q, k and v must share a dtype")
     if k_rope not in ("once", "per_tile"):
         raise ValueError("k_rope must be 'once' or 'per_tile'")
+    if k_rotated and (config is None or workspace is None or k_rope != "once"):
+        raise ValueError("k_rotated needs a configuration and the workspace holding the rotated K")
     if out_dtype is None:
         out_dtype = torch.float16 if q.dtype == torch.float8_e5m2 else q.dtype
     if out is None:
@@ -83,7 +87,8 @@ def prefill_gqa_rope(q, k, v, softmax_scale: float, causal: bool = True, rope_th
         else:
             code = _lib.lib().attn_prefill_gqa_rope(*args, _stream(stream))
     else:
-        code = _lib.lib().attn_prefill_gqa_rope_with_config(*args, int(config), ws_ptr, ws_bytes, _stream(stream))
+        cfg = int(config) | (_lib.ATTN_CONFIG_K_ROTATED if k_rotated else 0)
+        code = _lib.lib().attn_prefill_gqa_rope_with_config(*args, cfg, ws_ptr, ws_bytes, _stream(stream))
     _lib.check(code)
     return (out, lse) if return_lse else out
 

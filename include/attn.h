@@ -139,7 +139,14 @@ attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, const void* v
  * id (one configuration).  An id out of range returns ATTN_ERR_UNSUPPORTED.
  * With a NULL workspace K is rotated inside the kernel as in
  * attn_prefill_gqa_rope; with a workspace, once per key first, as in
- * attn_prefill_gqa_rope_ws. */
+ * attn_prefill_gqa_rope_ws.  ATTN_CONFIG_K_ROTATED or-ed into the id says
+ * that the workspace already holds this K rotated (left there by an earlier
+ * call with the same k, rope_theta and shapes): the rotation kernel is
+ * skipped and only the attention kernel runs, which times it on its own and
+ * lets calls that share K reuse the rotation (NULL workspace with the flag:
+ * ATTN_ERR_WORKSPACE; without RoPE, or for fp32 and fp8 inputs, the flag
+ * changes nothing). */
+#define ATTN_CONFIG_K_ROTATED 0x100
 int attn_prefill_num_configs(void);
 attn_status attn_prefill_gqa_rope_with_config(const void* q, const void* k, const void* v, void* o,
                                               float* lse, int B, int Hq, int Hkv, int S, int D,

@@ -83,6 +83,18 @@ def _prefill_ws(lib, ws=P, ws_bytes=None, **kw):
                                         a["theta"], a["qd"], a["kd"], a["vd"], ws, ws_bytes, None)
 
 
+def test_prefill_k_rotated_flag_needs_workspace(lib):
+    # ATTN_CONFIG_K_ROTATED says the workspace holds the rotated K: without one it is rejected on the host
+    code = lib.attn_prefill_gqa_rope_with_config(P, P, P, P2, None, 1, 4, 2, 16, 64, _lib.ATTN_BF16, _lib.ATTN_BF16,
+                                                 0.125, 1, 10000.0, 1.0, 1.0, 1.0, _lib.ATTN_CONFIG_K_ROTATED,
+                                                 None, 0, None)
+    assert code == 5
+    code = lib.attn_prefill_gqa_rope_with_config(P, P, P, P2, None, 1, 4, 2, 16, 64, _lib.ATTN_BF16, _lib.ATTN_BF16,
+                                                 0.125, 1, 10000.0, 1.0, 1.0, 1.0, _lib.ATTN_CONFIG_K_ROTATED | 7,
+                                                 P, 1 << 20, None)
+    assert code == 6  # configuration 7 does not exist
+
+
 def test_prefill_ws_workspace_size(lib):
     f = lib.attn_prefill_gqa_rope_workspace_bytes
     # rotated K: B * Hkv * S * D 16-bit elements

@@ -160,6 +160,27 @@ def test_prefill_persistent_equals_default(attn, B, Hq, Hkv, S, D, dtype, causal
     assert torch.equal(od, o0) and torch.equal(ld, l0)
 
 
+def test_prefill_k_rotated_flag_reuses_workspace(attn):
+    """ATTN_CONFIG_K_ROTATED: with the workspace left holding the rotated K by
+    a previous call, the attention kernel alone gives the two-kernel result
+    bit for bit; without a workspace the flag is rejected."""
+    B, Hq, Hkv, S, D = 1, 16, 4, 700, 128
+    q, k, v = _dev(*prefill_inputs(B, Hq, Hkv, S, D, "bf16", seed=21))
+    ws = torch.empty(attn.prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, q.dtype, 10000.0), dtype=torch.uint8,
+                     device="cuda")
+    o1, l1 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), rope_theta=10000.0, workspace=ws, config=0,
+                                   return_lse=True)
+    o2, l2 = attn.prefill_gqa_rope(q, k.flip(2).contiguous(), v, 1 / math.sqrt(D), rope_theta=10000.0,
+                                   workspace=ws, config=0, k_rotated=True, return_lse=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)  # (k itself was not read)
+    from attention_flash_attn_02_amd import _lib
+    ptr = [t.data_ptr() for t in (q, k, v, o1)]
+    code = _lib.lib().attn_prefill_gqa_rope_with_config(
+        *ptr, None, B, Hq, Hkv, S, D, _lib.ATTN_BF16, _lib.ATTN_BF16, 0.088, 1, 10000.0, 1.0, 1.0, 1.0,
+        _lib.ATTN_CONFIG_K_ROTATED, None, 0, torch.cuda.current_stream().cuda_stream)
+    assert code == 5
+
+
 def test_prefill_config_out_of_range(attn):
     q, k, v = _dev(*prefill_inputs(1, 2, 2, 16, 64, "bf16"))
     with pytest.raises(attn.AttnError):
