@@ -512,11 +512,18 @@ __device__ inline float pair_sum32(float x) {
 // sequence b is kv_len[b] (read on the device) and query row r sits at
 // position kv_len[b] - p.S + r (causal with that offset).
 // PERSIST: resident workgroups loop over several items (see below).
-template <class Tag, int D, bool CAUSAL, int ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false>
-__global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const PrefillParams p) {
+// BNT: keys per tile.  64 by default; 32 halves the LDS of a workgroup
+// (three workgroups, i.e. three waves per SIMD, fit a compute unit) and the
+// score registers, for the plain 4-wave kernel with K moved by DMA.
+template <class Tag, int D, bool CAUSAL, int ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false, int BNT = 64>
+__global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_kernel(const PrefillParams p) {
   static_assert(!CHUNK || (CAUSAL && !ROPE && HALVES == 1), "chunk mode: causal, no RoPE, 4 waves");
   static_assert(!PERSIST || (HALVES == 1 && !CHUNK), "persistent scheduling: 4 waves, plain prefill");
-  constexpr int BN = 64;
+  static_assert(BNT == 64 || (BNT == 32 && ROPE != 1 && HALVES == 1 && !CHUNK && !PERSIST),
+                "32-key tiles: plain 4-wave kernel with K moved by DMA");
+  constexpr int BN = BNT;
+  constexpr int NB = BN / 32;   // 32-key blocks of the score tile
+  constexpr int CPB = BN / 16;  // 16-key k-steps of the PV MFMAs
   constexpr int ROWB = D * 2;        // bytes per K/V row
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int TILEB = BN * ROWB;   // bytes of one K or V tile
@@ -784,15 +791,15 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
 
       if (active(i)) {
         // ---- S^T = K Q^T; A operands read from LDS three MFMAs ahead ----
-        f32x16 acc_s[2];
+        f32x16 acc_s[NB];
         {
           const uint8_t* kb = kbuf(i);
-          constexpr int NJ = 2 * NKK;  // MFMA j = NKK nb + kk
+          constexpr int NJ = NB * NKK;  // MFMA j = NKK nb + kk
           auto rd = [&](int j) {
             return *reinterpret_cast<const u32x4*>(kb + koff[j % NKK] + 32 * (j / NKK) * ROWB);
           };
-          acc_s[0] = f32x16{};
-          acc_s[1] = f32x16{};
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc_s[nb] = f32x16{};
           u32x4 fa[4];
           fa[0] = rd(0);
           fa[1] = rd(1);
@@ -820,14 +827,14 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
           // key = key0 + 4 hh + off(nb, r) is visible iff key <= min(qpos, S - 1)
           const int lim = (CAUSAL ? min(qoff + qpos, Skv - 1) : Skv - 1) - key0 - 4 * hh;
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (32 * nb + 8 * (r >> 2) + (r & 3) > lim) acc_s[nb][r] = kNegInf;
         }
         float mx = kNegInf;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[nb][r]);
         mx = pair_max32(mx) * p.scale_log2;
@@ -841,9 +848,9 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
           m_ref = m_new;
         }
         const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-        uint32_t pf[4][4];
+        uint32_t pf[CPB][4];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
             const float e0 = fast_exp2(fmaf(acc_s[nb][r], p.scale_log2, -m_use));
@@ -855,9 +862,9 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
         // ---- O^T += V^T P^T; transposing reads issued two MFMAs ahead ----
         {
           const uint8_t* vb = vbuf(i);
-          constexpr int NJ = NDB * 4;  // MFMA j = 4 db + c
+          constexpr int NJ = NDB * CPB;  // MFMA j = CPB db + c
           auto rd = [&](int j) {
-            const int db = j >> 2, c = j & 3;
+            const int db = j / CPB, c = j % CPB;
             const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16, vb + voff[db] + 16 * c * ROWB));
             const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16, vb + voff[db] + (16 * c + 8) * ROWB));
             const u32x2 a1 = __builtin_bit_cast(u32x2, x1), a2 = __builtin_bit_cast(u32x2, x2);
@@ -869,9 +876,9 @@ __global__ __launch_bounds__(256 * HALVES, 2) void prefill_fwd_kernel(const Pref
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             if (j + 2 < NJ) fa[(j + 2) % 3] = rd(j + 2);
-            const int c = j & 3;
+            const int c = j % CPB;
             const u32x4 bp = {pf[c][0], pf[c][1], pf[c][2], pf[c][3]};
-            acc_o[j >> 2] = Tag::mfma32(fa[j % 3], bp, acc_o[j >> 2]);
+            acc_o[j / CPB] = Tag::mfma32(fa[j % 3], bp, acc_o[j / CPB]);
           }
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -1560,9 +1567,25 @@ static void launch_pipe(const PrefillParams& p, bool causal, int rope, hipStream
   }
 }
 
+// configuration 4: the 4-wave kernel with 32-key tiles (three workgroups per
+// compute unit); RoPE with K rotated per staged tile has no such variant and
+// runs as configuration 0
+template <class Tag, int D>
+static void launch_bn32(const PrefillParams& p, bool causal, int rope, hipStream_t st) {
+  const dim3 grid((unsigned)((long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups)), block(256);
+  if (causal) {
+    if (rope == 2) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, 2, 1, false, false, 32>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, 0, 1, false, false, 32>), grid, block, 0, st, p);
+  } else {
+    if (rope == 2) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, 2, 1, false, false, 32>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, false, 0, 1, false, false, 32>), grid, block, 0, st, p);
+  }
+}
+
 template <class Tag, int D>
 static void launch_16bit(const PrefillParams& p, int config, bool causal, int rope, hipStream_t st) {
   if (config == 2) launch_pipe<Tag, D>(p, causal, rope, st);
+  else if (config == 4 && rope != 1) launch_bn32<Tag, D>(p, causal, rope, st);
   else launch_fwd<Tag, D>(p, causal, rope, st);  // 0, 1, 3 (persistent 4-wave)
 }
 
@@ -1697,7 +1720,10 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 //      residency rounds: two resident workgroups per compute unit loop over
 //      the items (snake order over the longest-first list); up to two rounds
 //      it launches as 0.
-static const int kPrefillConfigs = 4;
+//   4: the kernel of 0 with 32-key tiles: half the LDS and score registers,
+//      three workgroups (three waves per SIMD) per compute unit, two
+//      barriers per 64 keys (RoPE with K rotated per staged tile: as 0).
+static const int kPrefillConfigs = 5;
 static const int kPrefillGlobalConfig = 0;
 
 extern "C" size_t attn_prefill_gqa_rope_workspace_bytes(int B, int Hkv, int S, int D, attn_dtype in_dtype,

@@ -133,7 +133,9 @@ attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, const void* v
  * of this one); 3 = the kernel of 0 with persistent scheduling when the work
  * items exceed two residency rounds (two resident workgroups per compute
  * unit loop over the items, snake order over the longest-first list), and
- * launched as 0 otherwise.
+ * launched as 0 otherwise; 4 = the kernel of 0 with 32-key tiles (half the
+ * LDS, three workgroups per compute unit; RoPE with K rotated per staged
+ * tile runs as 0).
  * fp8 inputs: 1 = P in f16 with V upcast; every other id = P rounded to e4m3
  * for the PV MFMA (fp8 x bf8, twice the f16 rate).  fp32 inputs ignore the
  * id (one configuration).  An id out of range returns ATTN_ERR_UNSUPPORTED.

@@ -100,7 +100,7 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S, k_rope)
     assert _maxerr(lse, want_lse) <= 2e-2
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (4, 2)])
 @pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
                                                   (128, False, True, "f16"), (64, True, True, "bf16")])
@@ -109,7 +109,7 @@ def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype
     """Every tile configuration of the sweep passes parity before it is timed
     (GQA groups of 4, 1 and 2 query heads: different row layouts per wave),
     in both RoPE forms (K rotated once into the workspace, or per staged tile)."""
-    assert attn.prefill_num_configs() == 4
+    assert attn.prefill_num_configs() == 5
     if k_rope == "per_tile" and not rope:
         pytest.skip("no RoPE: both forms are the same launch")
     q, k, v = prefill_inputs(2, Hq, Hkv, 333, D, dtype, seed=config * 7 + D + Hq)
