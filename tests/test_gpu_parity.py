@@ -356,6 +356,26 @@ def test_decode_gqa_ragged_lengths(attn, split):
     assert torch.all(o[0].cpu() == 0)  # kv_len 0 -> zeros
 
 
+@pytest.mark.parametrize("cap,split,lengths", [(5, 32, [5, 1, 0, 3]), (33, 32, [33, 32, 1, 17]),
+                                              (200, 32, [200, 199, 97, 31, 0, 129]),
+                                              (130, 32, [130, 128, 96, 33, 65, 1]),
+                                              (4100, 1024, [4100, 4096, 4097, 1025, 2, 3000])])
+def test_decode_gqa_work_division(attn, cap, split, lengths):
+    """The workgroups of a KV head (ceil(cap / (4 split))) and their four
+    waves cut [0, kv_len) into equal runs of 32-slot chunks: caps below one
+    chunk, a chunk and one slot, several workgroups whose last waves get one
+    chunk or none, and a cap just past one workgroup's reach (partials plus
+    the combine); slots past each length hold NaN."""
+    q, kc, vc, L = decode_gqa_inputs(len(lengths), 16, 4, 128, cap, 0, "bf16", seed=cap + split,
+                                     nan_tail=True, lengths=lengths)
+    o = attn.decode_gqa(*_dev(q, kc, vc, L), 0.09, split=split)
+    want = oracle.decode_gqa(to_f64(q), to_f64(kc), to_f64(vc), L.numpy(), 0.09)
+    assert _maxerr(o, want) <= 2e-2
+    for i, n in enumerate(lengths):
+        if n == 0:
+            assert torch.all(o[i].cpu() == 0)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (16, 1), (12, 4)])
 def test_decode_gqa_group_sizes(attn, Hq, Hkv):
     q, kc, vc, L = decode_gqa_inputs(3, Hq, Hkv, 128, 400, 0, "f16", seed=Hq, lengths=[400, 333, 7])
