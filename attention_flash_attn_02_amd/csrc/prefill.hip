@@ -646,40 +646,6 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
     const int n = (n_kt + HALVES - 1) / HALVES;  // local tiles per half: local i is tile HALVES i + half
     const int qpos = pw0 + m;
 
-    // ---- Q fragments (B operand of S^T = K Q^T) ----
-    uint32_t qf[D / 4];
-    {
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head) * p.S + qpos) * D;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 w = qpos < p.S ? ldg16(qrow + 16 * kk + 8 * hh) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
-      }
-      if (RQ) {
-#pragma unroll
-        for (int kk = 0; kk < NKK / 2; ++kk)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w1 = qf[4 * kk + e], w2 = qf[4 * (kk + NKK / 2) + e];
-            float r1[2], r2[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              // angle in revolutions (v_sin/v_cos take revolutions)
-              const int fi = 16 * kk + 8 * hh + 2 * e + s;
-              const float rev = __builtin_amdgcn_fractf((float)qpos * p.rope_fhi[fi]) + (float)qpos * p.rope_flo[fi];
-              const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
-              const float x1 = Tag::to_f32(s ? (w1 >> 16) : (w1 & 0xffff));
-              const float x2 = Tag::to_f32(s ? (w2 >> 16) : (w2 & 0xffff));
-              r1[s] = x1 * cs - x2 * sn;
-              r2[s] = x2 * cs + x1 * sn;
-            }
-            qf[4 * kk + e] = Tag::pack2(r1[0], r1[1]);
-            qf[4 * (kk + NKK / 2) + e] = Tag::pack2(r2[0], r2[1]);
-          }
-      }
-    }
-
     const size_t kv_row0 = ((size_t)b * p.Hkv + kvh) * (CHUNK ? p.cap : p.S);
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k) + kv_row0 * ROWB;
     const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.v) + kv_row0 * ROWB;
@@ -775,6 +741,41 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
     } else if (exists(0)) {
       dma(kg, kbuf(0), dk, 0);
       dma(vg, vbuf(0), dv, 0);
+    }
+
+    // ---- Q fragments (B operand of S^T = K Q^T), loaded (and rotated) while
+    //      the first tile's K/V loads are in flight ----
+    uint32_t qf[D / 4];
+    {
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head) * p.S + qpos) * D;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 w = qpos < p.S ? ldg16(qrow + 16 * kk + 8 * hh) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
+      }
+      if (RQ) {
+#pragma unroll
+        for (int kk = 0; kk < NKK / 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w1 = qf[4 * kk + e], w2 = qf[4 * (kk + NKK / 2) + e];
+            float r1[2], r2[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              // angle in revolutions (v_sin/v_cos take revolutions)
+              const int fi = 16 * kk + 8 * hh + 2 * e + s;
+              const float rev = __builtin_amdgcn_fractf((float)qpos * p.rope_fhi[fi]) + (float)qpos * p.rope_flo[fi];
+              const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+              const float x1 = Tag::to_f32(s ? (w1 >> 16) : (w1 & 0xffff));
+              const float x2 = Tag::to_f32(s ? (w2 >> 16) : (w2 & 0xffff));
+              r1[s] = x1 * cs - x2 * sn;
+              r2[s] = x2 * cs + x1 * sn;
+            }
+            qf[4 * kk + e] = Tag::pack2(r1[0], r1[1]);
+            qf[4 * (kk + NKK / 2) + e] = Tag::pack2(r2[0], r2[1]);
+          }
+      }
     }
 
 #pragma unroll 1
