@@ -107,6 +107,59 @@ __global__ __launch_bounds__(256) void combine_kernel_v4s(const float* __restric
   if (lse_out && d == 0) lse_out[r] = mx + __log2f(wsum) * kLn2;
 }
 
+// Parts stored as bf16 bits (half the bytes of fp32 parts; used by the MLA
+// decode, whose parts are 448 wide): one thread per (row, 4 dims), the loop
+// of combine_kernel_v4 over 8-byte loads.
+__global__ __launch_bounds__(256) void combine_kernel_v4_bf16(const uint16_t* __restrict__ o_part,
+                                                              const float* __restrict__ lse_part,
+                                                              void* __restrict__ o, int R, int nsplit, int D,
+                                                              int out_dtype) {
+  const int d4n = D >> 2;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)R * d4n) return;
+  const int r = (int)(t / d4n), d = 4 * (int)(t % d4n);
+  const float* lse = lse_part + (size_t)r * nsplit;
+  float mx = kNegInf;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, lse[s]);
+  const size_t oidx = (size_t)r * D + d;
+  if (mx == kNegInf) {
+    store4(o, oidx, out_dtype, 0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const u32x2* op = reinterpret_cast<const u32x2*>(o_part + (size_t)r * nsplit * D + d);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  int s = 0;
+  for (; s + 4 <= nsplit; s += 4) {
+    u32x2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = op[(size_t)(s + u) * d4n];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = fast_exp2((lse[s + u] - mx) * kLog2e);
+      wsum += w;
+      acc += w * f32x4{Bf16Tag::to_f32(v[u][0] & 0xffff), Bf16Tag::to_f32(v[u][0] >> 16),
+                       Bf16Tag::to_f32(v[u][1] & 0xffff), Bf16Tag::to_f32(v[u][1] >> 16)};
+    }
+  }
+  for (; s < nsplit; ++s) {
+    const u32x2 v = op[(size_t)s * d4n];
+    const float w = fast_exp2((lse[s] - mx) * kLog2e);
+    wsum += w;
+    acc += w * f32x4{Bf16Tag::to_f32(v[0] & 0xffff), Bf16Tag::to_f32(v[0] >> 16), Bf16Tag::to_f32(v[1] & 0xffff),
+                     Bf16Tag::to_f32(v[1] >> 16)};
+  }
+  const float inv = 1.f / wsum;
+  store4(o, oidx, out_dtype, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+}
+
+void launch_combine_bf16_parts(const uint16_t* o_part, const float* lse_part, void* o, int R, int nsplit,
+                               int D, int out_dtype, hipStream_t stream) {
+  const long long threads = (long long)R * (D / 4);
+  hipLaunchKernelGGL(combine_kernel_v4_bf16, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, o_part,
+                     lse_part, o, R, nsplit, D, out_dtype);
+}
+
 // General D: one wave per row, four rows per workgroup.  Lane s holds split
 // s's weight (splits beyond 64 are folded in a loop), the weights are
 // broadcast with readlane, and the partial rows are read with independent

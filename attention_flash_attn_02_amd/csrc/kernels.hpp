@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace attn {
 
@@ -11,6 +12,10 @@ namespace attn {
 void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
                     int out_dtype, hipStream_t stream, float* lse_out = nullptr);
 
+// The same with the partial outputs stored as bf16 bits (o_part [R, nsplit, D]).
+void launch_combine_bf16_parts(const uint16_t* o_part, const float* lse_part, void* o, int R, int nsplit,
+                               int D, int out_dtype, hipStream_t stream);
+
 // Workspace layout of the decode calls: partial outputs first, then the
 // partial log-sum-exps, each 256-byte aligned.
 struct SplitWorkspace {
@@ -19,9 +24,9 @@ struct SplitWorkspace {
   size_t total;
 };
 
-inline SplitWorkspace split_workspace(long long rows, long long nsplit, long long d) {
+inline SplitWorkspace split_workspace(long long rows, long long nsplit, long long d, int part_bytes = 4) {
   SplitWorkspace w;
-  w.o_bytes = (size_t)(rows * nsplit * d) * sizeof(float);
+  w.o_bytes = (size_t)(rows * nsplit * d) * part_bytes;
   w.lse_offset = (w.o_bytes + 255) / 256 * 256;
   w.total = w.lse_offset + ((size_t)(rows * nsplit) * sizeof(float) + 255) / 256 * 256;
   return w;
