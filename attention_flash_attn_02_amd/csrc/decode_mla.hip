@@ -13,7 +13,7 @@
 // [128 w, 128 w + 128) of every cache row.  For each 32-slot chunk:
 //   * each wave streams its slice of the 32 rows into registers, whole rows
 //     per 16-lane group so that every L2 request is a full cache line (the
-//     next chunks' loads are in flight while the current one is computed);
+//     next chunk's loads are in flight while the current one is computed);
 //   * the slice rows are staged in the wave's LDS area; each wave computes
 //     S^T over its slice from 16-row fragments; the four partial score tiles
 //     are summed through LDS (one barrier per chunk), so every wave holds the
@@ -45,12 +45,16 @@ struct DecodeMlaParams {
 typedef __attribute__((ext_vector_type(4))) short v4i16_m;
 #define LDS_P(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
+// Chunk buffers per wave: two (one chunk in flight while one is computed)
+// keep the kernel at 145 VGPRs, so three workgroups (48 KB of LDS each) share
+// a compute unit; with four buffers and two workgroups per compute unit the
+// step was 1-10 % slower at every split size.
 #ifndef MLA_NBUF
-#define MLA_NBUF 4
+#define MLA_NBUF 2
 #endif
 
 template <class Tag, int NBUF = MLA_NBUF>
-__global__ __launch_bounds__(256, 2) void decode_mla_split_kernel(const DecodeMlaParams p) {
+__global__ __launch_bounds__(256, 3) void decode_mla_split_kernel(const DecodeMlaParams p) {
   constexpr int DQ = 512, DL = 448;
   constexpr int ROWB = 2 * DQ;     // bytes per cache row
   constexpr int SLB = 256;         // bytes of one wave's 128-dim slice of a row
