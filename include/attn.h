@@ -226,7 +226,8 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
  * Scores use all d_latent + d_rope dims; values are the latent part of the
  * same rows.  dtype: ATTN_BF16 or ATTN_F16.  d_latent = 448, d_rope = 64,
  * H <= 16.  split <= 0 picks the library default (256); otherwise a multiple
- * of 32 in [32, 2048].  Launches two kernels on `stream`.
+ * of 32 in [32, 2048], with ceil(cap / split) <= 65535 (else ATTN_ERR_SHAPE).
+ * Launches two kernels on `stream`.
  * ------------------------------------------------------------------------ */
 size_t attn_decode_mla_workspace_bytes(int B, int H, int cap, int d_latent, int split);
 attn_status attn_decode_mla(const void* q, const void* kv_cache, const int32_t* kv_len,

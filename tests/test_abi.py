@@ -188,6 +188,8 @@ def test_decode_mla_rejects(lib):
     assert _mla(lib, split=48) == 2
     assert _mla(lib, ws_bytes=16) == 5
     assert _mla(lib, c=ODD) == 4
+    # the split index is the second grid dimension: at most 65535 splits
+    assert _mla(lib, B=1, cap=32 * 65536, split=32) == 2
 
 
 def test_combine_rejects(lib):
