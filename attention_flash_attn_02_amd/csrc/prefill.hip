@@ -60,6 +60,7 @@ struct PrefillParams {
   float rope_fmid[64];  // three-way split (f_hi + f_mid + f_lo) for the fp32 kernel
   int halves;  // MFMA kernel: 1 = 4-wave workgroups, 2 = 8-wave split-key workgroups
   int persist;  // 4-wave kernel with resident workgroups looping over items (grid < items)
+  int pingpong;  // 8-wave kernel: the two halves run half a key tile apart (see PP)
   // chunked prefill against a cache prefix (prefill_fwd_kernel<..., CHUNK>)
   const int* kv_len;  // [B] key lengths including the chunk, device memory
   int cap;            // cache slots per head
@@ -515,12 +516,31 @@ __device__ inline float pair_sum32(float x) {
 // BNT: keys per tile.  64 by default; 32 halves the LDS of a workgroup
 // (three workgroups, i.e. three waves per SIMD, fit a compute unit) and the
 // score registers, for the plain 4-wave kernel with K moved by DMA.
-template <class Tag, int D, bool CAUSAL, int ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false, int BNT = 64>
+// PP (8-wave workgroups only): the halves' waves share SIMDs pairwise, and
+// with one barrier per key tile they would run the same phase at the same
+// time (both on the matrix cores, then both on the softmax ALU work).  With
+// PP each key tile has two barriers, one after the S MFMAs and one before
+// the PV MFMAs, and the second half passes one extra barrier before its key
+// loop (the first half one after it).  Every barrier instance then finds one
+// half between its two barriers (the softmax of a tile) and the other half
+// between the second and the next first (the PV MFMAs of a tile and the S
+// MFMAs of the next), so softmax work and MFMAs of the two halves overlap.
+// Each half's 4 waves still meet at one program point per instance, and each
+// half stages its own tiles, so the LDS protocol holds within each half: K
+// runs one tile ahead of V; each wave waits for its loads of V of tile i and
+// K of tile i+1 before the second barrier of tile i, and after its PV MFMAs
+// of tile i issues V of tile i+1 and K of tile i+2 into the stages of V(i-1)
+// and K(i), which every wave of the half finished reading before that
+// barrier.
+template <class Tag, int D, bool CAUSAL, int ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false, int BNT = 64,
+          bool PP = false>
 __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_kernel(const PrefillParams p) {
   static_assert(!CHUNK || (CAUSAL && !ROPE && HALVES == 1), "chunk mode: causal, no RoPE, 4 waves");
   static_assert(!PERSIST || (HALVES == 1 && !CHUNK), "persistent scheduling: 4 waves, plain prefill");
   static_assert(BNT == 64 || (BNT == 32 && ROPE != 1 && HALVES == 1 && !CHUNK && !PERSIST),
                 "32-key tiles: plain 4-wave kernel with K moved by DMA");
+  static_assert(!PP || (HALVES == 2 && ROPE != 1 && !CHUNK && !PERSIST && BNT == 64),
+                "offset halves: 8-wave kernel with K moved by DMA");
   constexpr int BN = BNT;
   constexpr int NB = BN / 32;   // 32-key blocks of the score tile
   constexpr int CPB = BN / 16;  // 16-key k-steps of the PV MFMAs
@@ -544,7 +564,11 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
   //   bank groups;  V, read transposed as 4 rows x 4 chunks per 32 lanes.
   auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
   auto vswz = [](int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // (8 waves: the wave index is read into a scalar register, so that the
+  // half's tile addresses are wave-uniform and its buffer loads take scalar
+  // descriptors directly instead of a loop over the distinct values)
+  const int tid = threadIdx.x, wave = HALVES == 2 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+  const int lane = tid & 63;
   const int half = HALVES == 2 ? wave >> 2 : 0, wq = wave & 3, htid = tid & 255;
   const int m = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, rr = lane & 15;
@@ -742,6 +766,7 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       dma(kg, kbuf(0), dk, 0);
       dma(vg, vbuf(0), dv, 0);
     }
+    if (PP && exists(1)) dma(kg, kbuf(1), dk, 1);  // K runs one tile ahead of V
 
     // ---- Q fragments (B operand of S^T = K Q^T), loaded (and rotated) while
     //      the first tile's K/V loads are in flight ----
@@ -778,6 +803,127 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       }
     }
 
+    if constexpr (PP) {
+      // the second half runs one barrier behind the first (see PP above);
+      // `lag` is wave-uniform and held in a scalar register, so the extra
+      // barriers are skipped by a scalar branch
+      const bool lag = __builtin_amdgcn_readfirstlane(half) == 1;
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // K(0), V(0), K(1) and the Q rows have landed
+      if (lag) asm volatile("s_barrier" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
+#pragma unroll 1
+      for (int i = 0; i < n; ++i) {
+        const bool act = active(i);
+        // ---- S^T = K Q^T (K of tile i landed before the previous second barrier) ----
+        f32x16 acc_s[NB];
+        if (act) {
+          const uint8_t* kb = kbuf(i);
+          constexpr int NJ = NB * NKK;
+          auto rd = [&](int j) {
+            return *reinterpret_cast<const u32x4*>(kb + koff[j % NKK] + 32 * (j / NKK) * ROWB);
+          };
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc_s[nb] = f32x16{};
+          u32x4 fa[4];
+          fa[0] = rd(0);
+          fa[1] = rd(1);
+          fa[2] = rd(2);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            if (j + 3 < NJ) fa[(j + 3) % 4] = rd(j + 3);
+            const int kk = j % NKK;
+            const u32x4 bq = {qf[4 * kk], qf[4 * kk + 1], qf[4 * kk + 2], qf[4 * kk + 3]};
+            acc_s[j / NKK] = Tag::mfma32(fa[j % 4], bq, acc_s[j / NKK]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            if (j + 3 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+          }
+        }
+        // first barrier: sets the phase of the two halves
+        asm volatile("s_barrier" ::: "memory");
+        // ---- mask, lazy online softmax ----
+        uint32_t pf[CPB][4];
+        if (act) {
+          const int key0 = (t0 + HALVES * i + half) * BN;
+          if ((key0 + BN > Skv) || (CAUSAL && key0 + BN - 1 > qoff + pw0)) {
+            asm volatile("" ::: "memory");
+            const int lim = (CAUSAL ? min(qoff + qpos, Skv - 1) : Skv - 1) - key0 - 4 * hh;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (32 * nb + 8 * (r >> 2) + (r & 3) > lim) acc_s[nb][r] = kNegInf;
+          }
+          float mx = kNegInf;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[nb][r]);
+          mx = pair_max32(mx) * p.scale_log2;
+          if (__ballot(mx > m_ref + kLazy)) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_ref - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+            m_ref = m_new;
+          }
+          const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              const float e0 = fast_exp2(fmaf(acc_s[nb][r], p.scale_log2, -m_use));
+              const float e1 = fast_exp2(fmaf(acc_s[nb][r + 1], p.scale_log2, -m_use));
+              const uint32_t pk = Tag::pack2(e0, e1);
+              pf[2 * nb + (r >> 3)][(r & 7) >> 1] = pk;
+              l_run = Tag::sum2(pk, l_run);
+            }
+        }
+        // second barrier: V(i) and K(i+1) of every wave of this half have
+        // landed, and every wave of the half is done with V(i-1) and K(i)
+        __builtin_amdgcn_s_waitcnt(0x3f70);
+        asm volatile("s_barrier" ::: "memory");
+        // ---- O^T += V^T P^T ----
+        if (act) {
+          const uint8_t* vb = vbuf(i);
+          constexpr int NJ = NDB * CPB;
+          auto rd = [&](int j) {
+            const int db = j / CPB, c = j % CPB;
+            const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16, vb + voff[db] + 16 * c * ROWB));
+            const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_AS(v4i16, vb + voff[db] + (16 * c + 8) * ROWB));
+            const u32x2 a1 = __builtin_bit_cast(u32x2, x1), a2 = __builtin_bit_cast(u32x2, x2);
+            return u32x4{a1[0], a1[1], a2[0], a2[1]};
+          };
+          u32x4 fa[3];
+          fa[0] = rd(0);
+          fa[1] = rd(1);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            if (j + 2 < NJ) fa[(j + 2) % 3] = rd(j + 2);
+            const int c = j % CPB;
+            const u32x4 bp = {pf[c][0], pf[c][1], pf[c][2], pf[c][3]};
+            acc_o[j / CPB] = Tag::mfma32(fa[j % 3], bp, acc_o[j / CPB]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        }
+        // V(i+1) and K(i+2) into the stages of V(i-1) and K(i).  Issued after
+        // the transposing reads of V(i): the compiler makes those reads wait
+        // for every LDS DMA in flight, so loads issued before them would
+        // stall the PV MFMAs until they land.
+        if (exists(i + 1)) dma(vg, vbuf(i + 1), dv, i + 1);
+        if (exists(i + 2)) dma(kg, kbuf(i + 2), dk, i + 2);
+      }
+      if (!lag) asm volatile("s_barrier" ::: "memory");
+    } else {
 #pragma unroll 1
     for (int i = 0; i < n; ++i) {
       __builtin_amdgcn_s_waitcnt(0x3f70);  // this thread's loads of tile i have landed
@@ -891,6 +1037,7 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       }
       if (RK && has_next) rotate_store_k(i + 1);
     }
+    }  // PP
 
     // ---- merge the two halves (same rows, disjoint key tiles) ----
     float* sc = reinterpret_cast<float*>(smem) + wq * (NDB * 16 + 2) * 64;
@@ -1532,6 +1679,13 @@ static void launch_fwd_hr(const PrefillParams& p, hipStream_t st) {
       return;
     }
   }
+  if constexpr (H == 2 && RM != 1) {
+    if (p.pingpong) {
+      hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, 2, false, false, 64, true>), dim3((unsigned)wgs),
+                         dim3(512), 0, st, p);
+      return;
+    }
+  }
   hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, H>), dim3((unsigned)wgs), dim3(256 * H), 0, st, p);
 }
 
@@ -1645,8 +1799,9 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   p.out_scale = v_descale;
   p.out_dtype = out_dtype;
   p.rope = rope ? 1 : 0;
-  p.halves = config == 1 ? 2 : 1;
+  p.halves = config == 1 || config == 5 ? 2 : 1;
   p.persist = config == 3 ? 1 : 0;
+  p.pingpong = config == 5 ? 1 : 0;
   if (rope && S > 65536) return ATTN_ERR_UNSUPPORTED;  // exact angle reduction needs pos < 2^16
   if (rope) {
     if (in_dtype == ATTN_F32) attn_host::rope_freq_split(rope_theta, D, p.inv_freq, p.rope_fhi, p.rope_flo, p.rope_fmid);
@@ -1723,8 +1878,11 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 //      it launches as 0.
 //   4: the kernel of 0 with 32-key tiles: half the LDS and score registers,
 //      three workgroups (three waves per SIMD) per compute unit, two
-//      barriers per 64 keys (RoPE with K rotated per staged tile: as 0).
-static const int kPrefillConfigs = 5;
+//      barriers per 64 keys (RoPE with K rotated per staged tile: as 0);
+//   5: the workgroups of 1 with the two halves half a key tile apart, so
+//      that one half's softmax overlaps the other's MFMAs (RoPE with K
+//      rotated per staged tile: as 1).
+static const int kPrefillConfigs = 6;
 static const int kPrefillGlobalConfig = 0;
 
 extern "C" size_t attn_prefill_gqa_rope_workspace_bytes(int B, int Hkv, int S, int D, attn_dtype in_dtype,

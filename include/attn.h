@@ -135,7 +135,9 @@ attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, const void* v
  * unit loop over the items, snake order over the longest-first list), and
  * launched as 0 otherwise; 4 = the kernel of 0 with 32-key tiles (half the
  * LDS, three workgroups per compute unit; RoPE with K rotated per staged
- * tile runs as 0).
+ * tile runs as 0); 5 = the workgroups of 1 with their halves run half a key
+ * tile apart, so that one half's softmax overlaps the other half's MFMAs
+ * (RoPE with K rotated per staged tile runs as 1).
  * fp8 inputs: 1 = P in f16 with V upcast; every other id = P rounded to e4m3
  * for the PV MFMA (fp8 x bf8, twice the f16 rate).  fp32 inputs ignore the
  * id (one configuration).  An id out of range returns ATTN_ERR_UNSUPPORTED.

@@ -100,7 +100,7 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S, k_rope)
     assert _maxerr(lse, want_lse) <= 2e-2
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (4, 2)])
 @pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
                                                   (128, False, True, "f16"), (64, True, True, "bf16")])
@@ -109,7 +109,7 @@ def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype
     """Every tile configuration of the sweep passes parity before it is timed
     (GQA groups of 4, 1 and 2 query heads: different row layouts per wave),
     in both RoPE forms (K rotated once into the workspace, or per staged tile)."""
-    assert attn.prefill_num_configs() == 5
+    assert attn.prefill_num_configs() == 6
     if k_rope == "per_tile" and not rope:
         pytest.skip("no RoPE: both forms are the same launch")
     q, k, v = prefill_inputs(2, Hq, Hkv, 333, D, dtype, seed=config * 7 + D + Hq)
@@ -120,6 +120,25 @@ def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype
                                     return_lse=True)
     assert _maxerr(o, want) <= TOL[dtype]
     assert _maxerr(lse, want_lse) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("config", [1, 5])
+@pytest.mark.parametrize("S", [1, 40, 64, 65, 128, 129, 192, 257, 320, 449])
+@pytest.mark.parametrize("D,causal,rope", [(128, True, True), (64, False, False), (128, True, False)])
+def test_prefill_split_key_tile_counts(attn, config, S, D, causal, rope):
+    """8-wave workgroups whose halves take alternate key tiles: with an odd
+    tile count the second half has one tile fewer, and causal workgroups
+    take a long and a short item in turn.  Configuration 5 runs the halves
+    half a tile apart with two barriers per tile; every wave must pass the
+    same number of barriers for every tile count."""
+    q, k, v = prefill_inputs(2, 8, 2, S, D, "bf16", seed=S + 3 * D + config)
+    theta = 10000.0 if rope else 0.0
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
+                                   config=config, return_lse=True)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta,
+                                    return_lse=True)
+    assert _maxerr(o, want) <= TOL["bf16"]
+    assert _maxerr(lse, want_lse) <= 2e-2
 
 
 @pytest.mark.parametrize("S", [1, 40, 64, 65, 128, 129, 192, 257])
