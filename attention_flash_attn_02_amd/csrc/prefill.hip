@@ -61,6 +61,7 @@ struct PrefillParams {
   int halves;  // MFMA kernel: 1 = 4-wave workgroups, 2 = 8-wave split-key workgroups
   int persist;  // 4-wave kernel with resident workgroups looping over items (grid < items)
   int pingpong;  // 8-wave kernel: the two halves run half a key tile apart (see PP)
+  int regstage;  // 4-wave kernel: K and V tiles staged through registers (see RS)
   // chunked prefill against a cache prefix (prefill_fwd_kernel<..., CHUNK>)
   const int* kv_len;  // [B] key lengths including the chunk, device memory
   int cap;            // cache slots per head
@@ -532,8 +533,14 @@ __device__ inline float pair_sum32(float x) {
 // of tile i issues V of tile i+1 and K of tile i+2 into the stages of V(i-1)
 // and K(i), which every wave of the half finished reading before that
 // barrier.
+// RS (4-wave workgroups only): K and V tiles go HBM -> registers -> LDS
+// (buffer loads after the loop-top barrier, swizzled LDS stores after the PV
+// MFMAs) instead of by DMA.  The compiler makes every transposing LDS read
+// wait for all LDS DMA in flight (`vmcnt(0)`), so with DMA the PV MFMAs of a
+// tile wait for the next tile's loads; register loads are waited for only
+// where their registers are stored.
 template <class Tag, int D, bool CAUSAL, int ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false, int BNT = 64,
-          bool PP = false>
+          bool PP = false, bool RS = false>
 __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_kernel(const PrefillParams p) {
   static_assert(!CHUNK || (CAUSAL && !ROPE && HALVES == 1), "chunk mode: causal, no RoPE, 4 waves");
   static_assert(!PERSIST || (HALVES == 1 && !CHUNK), "persistent scheduling: 4 waves, plain prefill");
@@ -541,6 +548,8 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
                 "32-key tiles: plain 4-wave kernel with K moved by DMA");
   static_assert(!PP || (HALVES == 2 && ROPE != 1 && !CHUNK && !PERSIST && BNT == 64),
                 "offset halves: 8-wave kernel with K moved by DMA");
+  static_assert(!RS || (HALVES == 1 && ROPE != 1 && !CHUNK && !PERSIST && BNT == 64 && !PP),
+                "register-staged tiles: plain 4-wave kernel");
   constexpr int BN = BNT;
   constexpr int NB = BN / 32;   // 32-key blocks of the score tile
   constexpr int CPB = BN / 16;  // 16-key k-steps of the PV MFMAs
@@ -692,6 +701,26 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       for (int u = 0; u < IPW; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_AS(void, dst + RPI * (wq * IPW + u) * ROWB), 16, loff[u], 0, 0, 0);
     };
+    // register staging (RS): this wave's IPW 16-byte chunks of a K tile and
+    // of a V tile, at the rows and chunks the DMA would move
+    u32x4 sreg[RS ? 2 * IPW : 1];
+    auto stage_load = [&](int i) {
+      const __amdgpu_buffer_rsrc_t ks = tile_rsrc(kg, i), vs = tile_rsrc(vg, i);
+#pragma unroll
+      for (int u = 0; u < IPW; ++u) {
+        const int off = (RPI * (wq * IPW + u) + lane / CH) * ROWB + 16 * (lane % CH);
+        sreg[u] = __builtin_amdgcn_raw_buffer_load_b128(ks, off, 0, 0);
+        sreg[IPW + u] = __builtin_amdgcn_raw_buffer_load_b128(vs, off, 0, 0);
+      }
+    };
+    auto stage_store = [&](int i) {
+#pragma unroll
+      for (int u = 0; u < IPW; ++u) {
+        const int row = RPI * (wq * IPW + u) + lane / CH, c = lane % CH;
+        *reinterpret_cast<u32x4*>(kbuf(i) + row * ROWB + 16 * (c ^ kswz(row))) = sreg[u];
+        *reinterpret_cast<u32x4*>(vbuf(i) + row * ROWB + 16 * (c ^ vswz(row))) = sreg[IPW + u];
+      }
+    };
     u32x4 kreg[RK ? 2 * PAIRS : 1];
     auto load_k_regs = [&](int i) {
       const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, i);
@@ -762,6 +791,8 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       }
       __syncthreads();
       if (exists(0)) rotate_store_k(0);
+    } else if (RS) {
+      if (exists(0)) stage_load(0);
     } else if (exists(0)) {
       dma(kg, kbuf(0), dk, 0);
       dma(vg, vbuf(0), dv, 0);
@@ -802,6 +833,8 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
           }
       }
     }
+
+    if (RS && exists(0)) stage_store(0);  // the loop-top barrier publishes it
 
     if constexpr (PP) {
       // the second half runs one barrier behind the first (see PP above);
@@ -930,9 +963,13 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       __syncthreads();                     // ... and everybody's; stage (i+1)&1 is free
       const bool has_next = exists(i + 1);
       if (has_next) {
-        dma(vg, vbuf(i + 1), dv, i + 1);
-        if (RK) load_k_regs(i + 1);
-        else dma(kg, kbuf(i + 1), dk, i + 1);
+        if (RS) {
+          stage_load(i + 1);
+        } else {
+          dma(vg, vbuf(i + 1), dv, i + 1);
+          if (RK) load_k_regs(i + 1);
+          else dma(kg, kbuf(i + 1), dk, i + 1);
+        }
       }
       if (RK) rope_base_fill(i + 2);
 
@@ -1036,6 +1073,7 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
         }
       }
       if (RK && has_next) rotate_store_k(i + 1);
+      if (RS && has_next) stage_store(i + 1);  // stage (i+1)&1: tile i-1, done by every wave
     }
     }  // PP
 
@@ -1679,6 +1717,13 @@ static void launch_fwd_hr(const PrefillParams& p, hipStream_t st) {
       return;
     }
   }
+  if constexpr (H == 1 && RM != 1) {
+    if (p.regstage) {
+      hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, 1, false, false, 64, false, true>),
+                         dim3((unsigned)wgs), dim3(256), 0, st, p);
+      return;
+    }
+  }
   if constexpr (H == 2 && RM != 1) {
     if (p.pingpong) {
       hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, CAUSAL, RM, 2, false, false, 64, true>), dim3((unsigned)wgs),
@@ -1802,6 +1847,7 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   p.halves = config == 1 || config == 5 ? 2 : 1;
   p.persist = config == 3 ? 1 : 0;
   p.pingpong = config == 5 ? 1 : 0;
+  p.regstage = config == 6 ? 1 : 0;
   if (rope && S > 65536) return ATTN_ERR_UNSUPPORTED;  // exact angle reduction needs pos < 2^16
   if (rope) {
     if (in_dtype == ATTN_F32) attn_host::rope_freq_split(rope_theta, D, p.inv_freq, p.rope_fhi, p.rope_flo, p.rope_fmid);
@@ -1881,8 +1927,10 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 //      barriers per 64 keys (RoPE with K rotated per staged tile: as 0);
 //   5: the workgroups of 1 with the two halves half a key tile apart, so
 //      that one half's softmax overlaps the other's MFMAs (RoPE with K
-//      rotated per staged tile: as 1).
-static const int kPrefillConfigs = 6;
+//      rotated per staged tile: as 1);
+//   6: the kernel of 0 with K and V tiles staged through registers instead
+//      of LDS DMA (RoPE with K rotated per staged tile: as 0).
+static const int kPrefillConfigs = 7;
 static const int kPrefillGlobalConfig = 0;
 
 extern "C" size_t attn_prefill_gqa_rope_workspace_bytes(int B, int Hkv, int S, int D, attn_dtype in_dtype,

@@ -137,7 +137,9 @@ attn_status attn_prefill_gqa_rope_ws(const void* q, const void* k, const void* v
  * LDS, three workgroups per compute unit; RoPE with K rotated per staged
  * tile runs as 0); 5 = the workgroups of 1 with their halves run half a key
  * tile apart, so that one half's softmax overlaps the other half's MFMAs
- * (RoPE with K rotated per staged tile runs as 1).
+ * (RoPE with K rotated per staged tile runs as 1); 6 = the kernel of 0 with
+ * the K and V tiles staged through registers instead of LDS DMA (RoPE with K
+ * rotated per staged tile runs as 0).
  * fp8 inputs: 1 = P in f16 with V upcast; every other id = P rounded to e4m3
  * for the PV MFMA (fp8 x bf8, twice the f16 rate).  fp32 inputs ignore the
  * id (one configuration).  An id out of range returns ATTN_ERR_UNSUPPORTED.

@@ -100,7 +100,7 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S, k_rope)
     assert _maxerr(lse, want_lse) <= 2e-2
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (4, 2)])
 @pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
                                                   (128, False, True, "f16"), (64, True, True, "bf16")])
@@ -109,7 +109,7 @@ def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype
     """Every tile configuration of the sweep passes parity before it is timed
     (GQA groups of 4, 1 and 2 query heads: different row layouts per wave),
     in both RoPE forms (K rotated once into the workspace, or per staged tile)."""
-    assert attn.prefill_num_configs() == 6
+    assert attn.prefill_num_configs() == 7
     if k_rope == "per_tile" and not rope:
         pytest.skip("no RoPE: both forms are the same launch")
     q, k, v = prefill_inputs(2, Hq, Hkv, 333, D, dtype, seed=config * 7 + D + Hq)
@@ -135,6 +135,21 @@ def test_prefill_split_key_tile_counts(attn, config, S, D, causal, rope):
     theta = 10000.0 if rope else 0.0
     o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
                                    config=config, return_lse=True)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta,
+                                    return_lse=True)
+    assert _maxerr(o, want) <= TOL["bf16"]
+    assert _maxerr(lse, want_lse) <= 2e-2
+
+
+@pytest.mark.parametrize("S", [1, 40, 64, 65, 128, 129, 192, 257])
+@pytest.mark.parametrize("D,causal,rope", [(128, True, True), (64, False, False), (128, False, True)])
+def test_prefill_register_staged_tile_counts(attn, S, D, causal, rope):
+    """Configuration 6 moves K and V tiles through registers: the first tile
+    in the prologue and every later one across the iteration before it."""
+    q, k, v = prefill_inputs(1, 8, 2, S, D, "bf16", seed=S + 5 * D)
+    theta = 10000.0 if rope else 0.0
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
+                                   config=6, return_lse=True)
     want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta,
                                     return_lse=True)
     assert _maxerr(o, want) <= TOL["bf16"]
