@@ -410,7 +410,7 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        log("bench.py measures one GPU only: this build has no multi-GPU path "
+        log("bench.py measures one GPU only: the library has no multi-GPU path "
             "(the prefill shards by KV-head group and decode by batch with no exchange).")
         sys.exit(2)
 

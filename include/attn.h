@@ -52,7 +52,7 @@ typedef enum attn_status {
     ATTN_ERR_DTYPE = 3,       /* unknown dtype or unsupported dtype combination */
     ATTN_ERR_ALIGN = 4,       /* a pointer is not suitably aligned             */
     ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required       */
-    ATTN_ERR_UNSUPPORTED = 6, /* valid request this build does not implement   */
+    ATTN_ERR_UNSUPPORTED = 6, /* valid request the library does not implement  */
     ATTN_ERR_LAUNCH = 7       /* the HIP runtime rejected a kernel launch      */
 } attn_status;
 
