@@ -482,6 +482,39 @@ def test_decode_workspace_reuse(attn):
         assert _maxerr(om, wantm) <= 2e-2
 
 
+@pytest.mark.parametrize("split", [0, 1024])
+def test_decode_mla_hipgraph_replay(attn, split):
+    """MLA decode (split kernel + combine of bf16 parts) captured in a hipGraph
+    replays bit-equal to the eager call; the default split leaves the ninth
+    split of the 2056-slot capacity empty.  A shorter length set in device
+    memory takes effect without re-capture."""
+    q, c, L = _dev(*decode_mla_inputs(8, 16, 448, 64, 2056, 2048, "bf16", seed=4))
+    ws = torch.empty(attn.decode_mla_workspace_bytes(8, 16, 2056, 448, split), dtype=torch.uint8, device="cuda")
+    out = torch.empty((8, 16, 448), dtype=torch.bfloat16, device="cuda")
+    eager = attn.decode_mla(q, c, L, 0.072, split=split, workspace=ws).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        attn.decode_mla(q, c, L, 0.072, split=split, out=out, workspace=ws)  # warm up on the side stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            attn.decode_mla(q, c, L, 0.072, split=split, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        _ = (q.float() * 2).sum()  # unrelated eager work between replays
+    L.fill_(700)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, attn.decode_mla(q, c, L, 0.072, split=split))
+    want = oracle.decode_mla(to_f64(q), to_f64(c), L.cpu().numpy(), 0.072, 448)
+    assert _maxerr(out, want) <= 2e-2
+
+
 @pytest.mark.parametrize("B", [1, 32, 128])
 def test_decode_mla_config(attn, B):
     """Absorbed-MLA decode: H=16, latent 448 + rope 64, context 2048 in
