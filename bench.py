@@ -1,15 +1,16 @@
 """Benchmark of the attention forward hot path on one MI355X.
 
 A step is one causal GQA prefill with fused RoPE at the full workload
-(B=1, Hq=32, Hkv=8, S=2048, D=128, bf16 in and out, theta 10000): one launch
-of the prefill kernel.  ``value`` is its throughput in useful TFLOP/s
+(B=1, Hq=32, Hkv=8, S=2048, D=128, bf16 in and out, theta 10000): the K
+rotation into the workspace, then the attention kernel, which rotates its Q
+rows in registers.  ``value`` is its throughput in useful TFLOP/s
 (4 * B * Hq * D * S(S+1)/2 flops per step, masked work excluded), with inputs
 resident in HBM.  The same JSON line carries the roofline of that kernel, the
 CPU float64 oracle timed on a bounded sample of the same workload, and the
 other paths (GQA and MLA decode in eager and hipGraph modes, MHA forward in
 fp16 / fp8, the tiny fp32 prefill) as secondary figures.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick [--prefill-config N]]
 """
 from __future__ import annotations
 
@@ -406,9 +407,15 @@ def main():
                          "each (for profiling runs); prints one JSON line of its own")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true", help="skip the tile-config sweep")
+    ap.add_argument("--prefill-config", type=int, default=None,
+                    help="profiling runs only (with --quick): run the prefill step in this sweep "
+                         "configuration instead of the global one")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+    if args.prefill_config is not None and not args.quick:
+        log("--prefill-config is for profiling runs and needs --quick")
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("bench.py measures one GPU only: the library has no multi-GPU path "
             "(the prefill shards by KV-head group and decode by batch with no exchange).")
@@ -449,8 +456,10 @@ def main():
     ws = torch.empty(attn.prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, torch.bfloat16, 10000.0),
                      dtype=torch.uint8, device=dev)
 
+    cfg = args.prefill_config  # None: the global configuration (attn_prefill_gqa_rope_ws)
+
     def step():
-        attn.prefill_gqa_rope(q, k, v, scale, causal=True, rope_theta=10000.0, out=out, workspace=ws)
+        attn.prefill_gqa_rope(q, k, v, scale, causal=True, rope_theta=10000.0, out=out, workspace=ws, config=cfg)
 
     for _ in range(args.warmup):
         step()
@@ -469,7 +478,8 @@ def main():
     # kernel is skipped; HIP events on the same stream.  The rest of the step
     # is the K rotation and its launch.
     ms_kern = time_loop(lambda: attn.prefill_gqa_rope(q, k, v, scale, causal=True, rope_theta=10000.0, out=out,
-                                                      workspace=ws, config=0, k_rotated=True),
+                                                      workspace=ws, config=0 if cfg is None else cfg,
+                                                      k_rotated=True),
                         args.steps, args.warmup)
     ms_pre = ms - ms_kern
     kern_tflops = flops / (ms_kern * 1e-3) / 1e12
@@ -488,7 +498,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": prefill_traffic(),
-                     "kernel": "prefill_fwd_kernel<bf16,128,causal,RoPE on Q (K rotated once),4 waves>",
+                     "kernel": "prefill_fwd_kernel<bf16,128,causal,RoPE on Q (K rotated once),4 waves>"
+                               if cfg is None else f"prefill configuration {cfg}",
                      "kernel_us": round(ms_kern * 1e3, 2), "k_rotation_us": round(ms_pre * 1e3, 2),
                      "algorithmic_per_launch": flops},
     }

@@ -40,3 +40,12 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_prefill_config_override_needs_quick():
+    # a sweep configuration may only replace the global one in profiling runs
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--prefill-config", "1"], cwd=ROOT,
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--quick" in r.stderr
+    assert r.stdout == ""
