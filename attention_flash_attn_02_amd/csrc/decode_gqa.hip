@@ -63,7 +63,10 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_gqa_kernel(const DecodeGqaP
   // per wave: V rows and K rows of the chunk (reused for the merge)
   __shared__ __attribute__((aligned(1024))) uint8_t stage[NW][2][32 * ROWB];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index in a scalar register: the wave's slot range, and with it
+  // the K/V buffer descriptors, are then wave-uniform, and the buffer loads
+  // take them as they are instead of looping over distinct per-lane values
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint8_t* vs = stage[wave][0];
   uint8_t* ks = stage[wave][1];
   const int m16 = lane & 15, qq = lane >> 4;
