@@ -61,9 +61,11 @@ __global__ __launch_bounds__(256) void combine_kernel_v4(const float* __restrict
 }
 
 // The same for at most NS parts: every lse and every float4 of the row's
-// parts is loaded up front (raw buffer loads whose range ends at the row's
-// last part, so loads past it return zero without a branch), which leaves
-// one memory round trip per thread instead of one per group of parts.
+// parts is loaded up front, which leaves one memory round trip per thread
+// instead of one per group of parts.  The buffer descriptors cover the whole
+// part and lse arrays (the same for every lane, so the loads take them as
+// they are): a load for a split s >= nsplit reads the next row's values,
+// which get weight 0, or, past the last row, zero without a memory access.
 template <int NS>
 __global__ __launch_bounds__(256) void combine_kernel_v4s(const float* __restrict__ o_part,
                                                           const float* __restrict__ lse_part,
@@ -73,16 +75,17 @@ __global__ __launch_bounds__(256) void combine_kernel_v4s(const float* __restric
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   if (t >= (long long)R * d4n) return;
   const int r = (int)(t / d4n), d = 4 * (int)(t % d4n);
-  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(lse_part + (size_t)r * nsplit), (short)0, nsplit * 4, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(o_part + (size_t)r * nsplit * D), (short)0, nsplit * D * 4, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lse_part), (short)0, R * nsplit * 4, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ors =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(o_part), (short)0, R * nsplit * D * 4, kBufferRsrcWord3);
+  const int l0 = 4 * r * nsplit, o0 = 4 * (r * nsplit * D + d);  // byte offsets of split 0
   float l[NS];
   f32x4 v[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    l[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, 4 * s, 0, 0));
-    v[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, 4 * (s * D + d), 0, 0));
+    l[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, l0 + 4 * s, 0, 0));
+    v[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, o0 + 4 * s * D, 0, 0));
   }
   float mx = kNegInf;
 #pragma unroll
@@ -98,9 +101,11 @@ __global__ __launch_bounds__(256) void combine_kernel_v4s(const float* __restric
   float wsum = 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const float w = s < nsplit ? fast_exp2((l[s] - mx) * kLog2e) : 0.f;
-    wsum += w;
-    acc += w * v[s];
+    if (s < nsplit) {  // (a uniform branch: loads past the row read other rows' values, never used)
+      const float w = fast_exp2((l[s] - mx) * kLog2e);
+      wsum += w;
+      acc += w * v[s];
+    }
   }
   const float inv = 1.f / wsum;
   store4(o, oidx, out_dtype, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
@@ -217,11 +222,12 @@ void launch_combine(const float* o_part, const float* lse_part, void* o, int R, 
   if (D % 4 == 0) {
     const long long threads = (long long)R * (D / 4);
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-    // (buffer ranges are 32-bit: a row's parts must span less than 2 GiB)
+    // (buffer ranges and offsets are 32-bit: all parts, plus the loads past
+    // the last row's, must span less than 2 GiB)
     // up to 8 parts: every load up front (GQA decode's five parts: 5.1 -> 4.7 us
     // at batch 128); more parts: the loop (loading 16 slots for MLA's nine
     // parts was slower, 8.9 vs 7.6 us)
-    if (nsplit <= 8 && (long long)nsplit * D * 4 < (1LL << 31))
+    if (nsplit <= 8 && ((long long)R * nsplit + 8) * D * 4 < (1LL << 31))
       hipLaunchKernelGGL(combine_kernel_v4s<8>, grid, block, 0, stream, o_part, lse_part, o, lse_out, R, nsplit, D,
                          out_dtype);
     else

@@ -558,6 +558,21 @@ def test_combine_matches_pairwise_merge(attn, D, ns, empty):
     assert _maxerr(got, want) <= 1e-5
 
 
+@pytest.mark.parametrize("ns", [1, 3, 5, 8])
+def test_combine_rows_do_not_mix(attn, ns):
+    """With up to 8 parts every part is loaded up front, including slots past
+    a row's last split, which hold the next row's values: rows whose parts are
+    NaN or infinite must not leak into their neighbours."""
+    o_part, lse = split_partials(6, ns, 128, seed=ns + 40)
+    o_part[1] = float("nan")
+    o_part[3, :, :64] = float("inf")
+    lse[3, 0] = float("nan")
+    got = attn.combine_splits(*_dev(o_part, lse)).cpu()
+    keep = [0, 2, 4, 5]
+    want = oracle.combine_splits(o_part[keep].numpy(), lse[keep].numpy())
+    assert _maxerr(got[keep], want) <= 1e-5
+
+
 @pytest.mark.parametrize("ns", [3, 12, 20])
 def test_combine_all_parts_empty(attn, ns):
     """A row whose parts are all empty (lse -inf) is written as zeros."""
