@@ -573,10 +573,11 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
   //   bank groups;  V, read transposed as 4 rows x 4 chunks per 32 lanes.
   auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
   auto vswz = [](int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
-  // (8 waves: the wave index is read into a scalar register, so that the
-  // half's tile addresses are wave-uniform and its buffer loads take scalar
-  // descriptors directly instead of a loop over the distinct values)
-  const int tid = threadIdx.x, wave = HALVES == 2 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+  // (8 waves and chunk mode: the wave index is read into a scalar register,
+  // so that the tile addresses are wave-uniform and the buffer loads take
+  // scalar descriptors directly instead of a loop over the distinct values;
+  // the plain 4-wave kernel measured slower that way and keeps tid >> 6)
+  const int tid = threadIdx.x, wave = (HALVES == 2 || CHUNK) ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int lane = tid & 63;
   const int half = HALVES == 2 ? wave >> 2 : 0, wq = wave & 3, htid = tid & 255;
   const int m = lane & 31, hh = lane >> 5;
