@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
 // softmax and O^T += V^T P^T for its current tile.  MFMA operands are read
 // from LDS a few MFMAs ahead of their use.
 //
-// K and V tiles go straight from HBM to LDS (global_load_lds, 16 B per lane)
+// K and V tiles go straight from HBM to LDS (buffer loads with the LDS bit, 16 B per lane)
 // into XOR-swizzled row-major layouts, two stages per tensor per half.  V is
 // read transposed by ds_read_b64_tr_b16: each 16-lane group reads a 4-key x
 // 16-dim block and every lane receives one dim column of 4 keys, which is
