@@ -95,6 +95,15 @@ def test_prefill_k_rotated_flag_needs_workspace(lib):
     assert code == 6  # configuration 7 does not exist
 
 
+def test_prefill_config_ids(lib):
+    # ids 0..6 are the sweep configurations (0 the global one); anything else is rejected on the host
+    assert lib.attn_prefill_num_configs() == 7
+    for bad in (-1, 7, 1000):
+        code = lib.attn_prefill_gqa_rope_with_config(P, P, P, P2, None, 1, 4, 2, 16, 64, _lib.ATTN_BF16,
+                                                     _lib.ATTN_BF16, 0.125, 1, 0.0, 1.0, 1.0, 1.0, bad, None, 0, None)
+        assert code == 6
+
+
 def test_prefill_ws_workspace_size(lib):
     f = lib.attn_prefill_gqa_rope_workspace_bytes
     # rotated K: B * Hkv * S * D 16-bit elements
