@@ -28,6 +28,12 @@ COMMON_FLAGS = [
 ]
 
 
+# per-source flags.  prefill_sp.hip: select the VGPR form of the MFMAs, so
+# the score tiles the softmax reads stay in VGPRs (with accumulation
+# registers the compiler keeps copying them back and forth).
+SOURCE_FLAGS = {"prefill_sp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(line for line in r.stdout.splitlines()
@@ -44,7 +50,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in sources]
     jobs = jobs or min(8, len(sources), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [HIPCC, *COMMON_FLAGS, "-c", s, "-o", o]) for s, o in zip(sources, objs)]
+        futs = [ex.submit(_run, [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o])
+                for s, o in zip(sources, objs)]
         for f in futs:
             out = f.result()
             if verbose and out.strip():

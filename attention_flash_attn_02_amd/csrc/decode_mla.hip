@@ -252,7 +252,8 @@ extern "C" attn_status attn_decode_mla(const void* q, const void* kv_cache, cons
   split = mla_split(split);
   if (split % 32 != 0 || split < 32 || split > 2048) return ATTN_ERR_SHAPE;
   if (B > 65535) return ATTN_ERR_SHAPE;
-  if (!(softmax_scale == softmax_scale)) return ATTN_ERR_SHAPE;
+  // the score scale must be a positive finite number, as for the prefill
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 3.0e38f)) return ATTN_ERR_SHAPE;
   if (!attn_host::aligned(q, 16) || !attn_host::aligned(kv_cache, 16) ||
       !attn_host::aligned(o, 16) || !attn_host::aligned(kv_len, 4))
     return ATTN_ERR_ALIGN;

@@ -31,45 +31,11 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "prefill_common.hpp"
 
 namespace attn {
 
-struct PrefillParams {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* o;
-  float* lse;
-  int B, Hq, Hkv, S;
-  int G;          // Hq / Hkv
-  int GP;         // heads of one KV group handled by one workgroup
-  int P;          // query positions per workgroup
-  int n_ptiles;   // ceil(S / P)
-  int n_hgroups;  // G / GP
-  float scale_log2;  // softmax_scale * q_descale * k_descale * log2(e)
-  float out_scale;   // v_descale
-  int out_dtype;
-  int rope;
-  float inv_freq[64];  // RoPE inverse frequencies theta^(-2i/D), i < D/2
-  // RoPE frequencies in revolutions per position, f = theta^(-2i/D) / (2 pi),
-  // split as f_hi + f_lo with f_hi carrying 8 significant bits: pos * f_hi is
-  // then exact in fp32 for pos < 2^16, so frac(pos * f_hi) + pos * f_lo gives
-  // the angle modulo one revolution to ~1e-7 without fp64 arithmetic.
-  float rope_fhi[64];
-  float rope_flo[64];
-  float rope_fmid[64];  // three-way split (f_hi + f_mid + f_lo) for the fp32 kernel
-  int halves;  // MFMA kernel: 1 = 4-wave workgroups, 2 = 8-wave split-key workgroups
-  int persist;  // 4-wave kernel with resident workgroups looping over items (grid < items)
-  int pingpong;  // 8-wave kernel: the two halves run half a key tile apart (see PP)
-  int regstage;  // 4-wave kernel: K and V tiles staged through registers (see RS)
-  // chunked prefill against a cache prefix (prefill_fwd_kernel<..., CHUNK>)
-  const int* kv_len;  // [B] key lengths including the chunk, device memory
-  int cap;            // cache slots per head
-  int nsplit;         // key ranges per item (1: results go straight to o / lse)
-  int split_keys;     // keys per range, a multiple of 64
-  float* ws_o;        // [B*Hq*S, nsplit, D] partial outputs (nsplit > 1)
-  float* ws_lse;      // [B*Hq*S, nsplit] partial log-sum-exps (nsplit > 1)
-};
+
 
 // ---------------------------------------------------------------------------
 // MFMA kernel
@@ -495,20 +461,6 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
 // maximum is only moved when a row's maximum exceeds it by more than 2^8
 // (lazy rescaling: exact, the probabilities just stay below 256).
 // ---------------------------------------------------------------------------
-typedef __attribute__((ext_vector_type(4))) short v4i16;
-#define LDS_AS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
-
-// max / sum of x over lanes l and l ^ 32: v_permlane32_swap of x with itself
-// leaves one copy of x and one copy of the partner's x in the two results.
-__device__ inline float pair_max32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float pair_sum32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // CHUNK: the queries are a chunk of p.S rows at the end of a cache prefix:
 // K/V rows come from caches with p.cap slots per head, the key length of
 // sequence b is kv_len[b] (read on the device) and query row r sits at
@@ -1840,6 +1792,7 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
   PrefillParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.S = S;
+  p.D = D;
   p.G = Hq / Hkv;
   p.scale_log2 = softmax_scale * q_descale * k_descale * kLog2e;
   p.out_scale = v_descale;
@@ -1889,6 +1842,14 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
     p.k = workspace;
     rope_mode = 2;
   }
+  // configurations 7 and 8: the software-pipelined kernel (4- and 8-wave
+  // workgroups); RoPE on K per staged tile is not built into it and runs as
+  // configuration 0
+  if ((config == 7 || config == 8) && rope_mode != 1 && (in_dtype == ATTN_BF16 || in_dtype == ATTN_F16)) {
+    launch_prefill_sp(p, in_dtype == ATTN_BF16, c, rope_mode == 2, config == 8 ? 2 : 1, stream);
+    return attn_host::launch_status();
+  }
+  if (config == 7 || config == 8) config = 0;
   switch (in_dtype) {
     case ATTN_BF16:
       if (D == 64) launch_16bit<Bf16Tag, 64>(p, config, c, rope_mode, stream);
@@ -1914,8 +1875,9 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 // Tile configurations of the 16-bit MFMA prefill kernel (fp32 inputs have a
 // single configuration; fp8 inputs use 1 for P in f16 and the default
 // otherwise):
-//   0 (global default): 4-wave workgroups, 128 query rows, 64-key tiles, one
-//      workgroup per work item;
+//   0: 4-wave workgroups (two per compute unit), 128 query rows, 64-key
+//      tiles, one workgroup per work item (the fp8 default, and the kernel
+//      for RoPE with K rotated per staged tile);
 //   1: 8-wave workgroups whose two halves split the key tiles of 128 rows;
 //   2: the tiling of 0, software-pipelined (S of the next tile overlaps the
 //      softmax of this one);
@@ -1930,9 +1892,17 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 //      that one half's softmax overlaps the other's MFMAs (RoPE with K
 //      rotated per staged tile: as 1);
 //   6: the kernel of 0 with K and V tiles staged through registers instead
-//      of LDS DMA (RoPE with K rotated per staged tile: as 0).
-static const int kPrefillConfigs = 7;
-static const int kPrefillGlobalConfig = 0;
+//      of LDS DMA (RoPE with K rotated per staged tile: as 0);
+//   7 (global default for 16-bit inputs): the software-pipelined kernel
+//      (prefill_sp.hip): 4-wave workgroups, the S MFMAs of the next key tile
+//      interleaved with the softmax of this one and the PV MFMAs with the
+//      rest of it, K/V tiles loaded an iteration ahead into per-stage LDS
+//      arrays, causal items paired long with short in one workgroup (RoPE
+//      with K rotated per staged tile: as 0);
+//   8: the kernel of 7 with 8-wave workgroups whose halves take alternate key
+//      tiles of the same rows (two waves per SIMD with half the items).
+static const int kPrefillConfigs = 9;
+static const int kPrefillGlobalConfig = 7;
 
 extern "C" size_t attn_prefill_gqa_rope_workspace_bytes(int B, int Hkv, int S, int D, attn_dtype in_dtype,
                                                        float rope_theta) {

@@ -48,6 +48,8 @@ def mla_decode_bytes(B, H=16, dq=512, dl=448, L=2048, elem=2):
     return B * (L * dq * elem + H * dq * elem + H * dl * elem)
 
 
+GLOBAL_CONFIG = 7  # the library's global 16-bit prefill configuration (what the calls without one use)
+
 SPIN_S = 0.06  # untimed work before each measurement: the clock takes ~45 ms of load to settle
 
 
@@ -286,22 +288,32 @@ SWEEP_ROUNDS = 3
 def sweep(scale):
     """Every tile configuration per shape; gap of the global configuration to the best one.
 
-    Prefill: attn_prefill_gqa_rope_with_config ids (global = 0), timed in
+    Prefill: attn_prefill_gqa_rope_with_config ids (the global one is
+    GLOBAL_CONFIG for 16-bit inputs; fp8 inputs have two configurations, 0
+    with P in e4m3 (their default) and 1 with P in f16), timed in
     SWEEP_ROUNDS interleaved rounds (seeded random order), median per
-    configuration.  Decode: the
-    split size (global = the library default), hipGraph mode, cold caches."""
+    configuration.  Decode: the split size (global = the library default),
+    hipGraph mode, cold caches."""
     import torch
     import attention_flash_attn_02_amd as attn
     from workloads import prefill_inputs
     dev = torch.device("cuda:0")
     out = {}
     nconf = attn.prefill_num_configs()
-    shapes = [("C2_gqa_rope_bf16_S2048", (1, 32, 8, 2048, 128, "bf16", True, 10000.0, torch.bfloat16)),
-              ("mha_D64_noncausal_N4096_f16", (4, 32, 32, 4096, 64, "f16", False, 0.0, torch.float16)),
-              ("mha_D128_causal_N4096_f16", (4, 32, 32, 4096, 128, "f16", True, 0.0, torch.float16)),
-              ("mha_D128_causal_N16384_f16", (4, 32, 32, 16384, 128, "f16", True, 0.0, torch.float16)),
-              ("mha_D64_noncausal_N1024_f16", (4, 32, 32, 1024, 64, "f16", False, 0.0, torch.float16))]
-    for name, (B, Hq, Hkv, S, D, dt, causal, theta, odt) in shapes:
+    all16 = list(range(nconf))
+    shapes = [("C2_gqa_rope_bf16_S2048", (1, 32, 8, 2048, 128, "bf16", True, 10000.0, torch.bfloat16), all16, GLOBAL_CONFIG),
+              ("mha_D64_noncausal_N4096_f16", (4, 32, 32, 4096, 64, "f16", False, 0.0, torch.float16), all16, GLOBAL_CONFIG),
+              ("mha_D128_causal_N4096_f16", (4, 32, 32, 4096, 128, "f16", True, 0.0, torch.float16), all16, GLOBAL_CONFIG),
+              ("mha_D128_causal_N16384_f16", (4, 32, 32, 16384, 128, "f16", True, 0.0, torch.float16), all16,
+               GLOBAL_CONFIG),
+              ("mha_D64_noncausal_N1024_f16", (4, 32, 32, 1024, 64, "f16", False, 0.0, torch.float16), all16,
+               GLOBAL_CONFIG),
+              ("mha_D128_causal_N2048_f16", (4, 32, 32, 2048, 128, "f16", True, 0.0, torch.float16), all16, GLOBAL_CONFIG),
+              ("mha_D64_noncausal_N8192_f16", (4, 32, 32, 8192, 64, "f16", False, 0.0, torch.float16), all16,
+               GLOBAL_CONFIG),
+              ("mha_D64_noncausal_N4096_fp8", (4, 32, 32, 4096, 64, "fp8_e5m2", False, 0.0, torch.float16), [0, 1], 0),
+              ("mha_D128_causal_N4096_fp8", (4, 32, 32, 4096, 128, "fp8_e5m2", True, 0.0, torch.float16), [0, 1], 0)]
+    for name, (B, Hq, Hkv, S, D, dt, causal, theta, odt), confs, glob in shapes:
         q, k, v = [t.to(dev) for t in prefill_inputs(B, Hq, Hkv, S, D, dt, seed=S)]
         o = torch.empty(q.shape, dtype=odt, device=dev)
         ws = torch.empty(max(1, attn.prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, q.dtype, theta)),
@@ -309,9 +321,9 @@ def sweep(scale):
         it = 20 if S <= 4096 else 4
         # configurations interleaved over rounds in a seeded random order, median per configuration
         rng = random.Random(S * 7 + D)
-        samples = {c: [] for c in range(nconf)}
+        samples = {c: [] for c in confs}
         for rnd in range(SWEEP_ROUNDS):
-            order = list(range(nconf))
+            order = list(confs)
             rng.shuffle(order)
             for c in order:
                 ms = time_loop(lambda: attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal,
@@ -320,8 +332,9 @@ def sweep(scale):
                 samples[c].append(ms)
         times = {str(c): round(sorted(v)[len(v) // 2] * 1e3, 2) for c, v in samples.items()}
         best = min(times.values())
-        out["prefill_" + name] = {"us": times, "global": "0", "best": min(times, key=times.get),
-                                  "gap_pct": round(100 * (times["0"] / best - 1), 2)}
+        g = str(glob)
+        out["prefill_" + name] = {"us": times, "global": g, "best": min(times, key=times.get),
+                                  "gap_pct": round(100 * (times[g] / best - 1), 2)}
         del q, k, v, o, ws
     for kind, Bs, sc in (("gqa", (1, 8, 32, 64, 128), scale), ("mla", (1, 32, 128), 1 / math.sqrt(192))):
         for Bd in Bs:
@@ -370,11 +383,26 @@ def cpu_baseline(budget_s=15.0):
     """Time the float64 oracle on KV groups of the full prefill workload until
     about `budget_s` seconds of CPU work (or the whole workload) is done."""
     import numpy as np
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in pools] or [1])
+        if pools:
+            p = pools[0]
+            blas = f"{p.get('internal_api', '?')} {p.get('version', '?')} ({p.get('threading_layer', '?')} threads, " \
+                   f"{p.get('architecture', '?')})"
     except Exception:  # pragma: no cover
         threads = 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     import oracle
     from workloads import prefill_inputs, to_f64
     q, k, v = prefill_inputs(1, 32, 8, 2048, 128, "bf16")
@@ -389,8 +417,9 @@ def cpu_baseline(budget_s=15.0):
             break
     dt = time.perf_counter() - t0
     flops = prefill_flops(1, 4 * groups, 2048, 128, True)
-    del np
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model, "host_cpus": len(os.sched_getaffinity(0)), "blas": blas,
+            "numpy": np.__version__,
             "sample": f"{groups} of 8 KV groups ({4 * groups} of 32 query heads) of the causal GQA "
                       f"RoPE prefill B=1 S=2048 D=128, float64 numpy, {dt:.2f} s"}
 
@@ -463,6 +492,9 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # untimed steps until the clock has settled under load (it takes ~45 ms of
+    # back-to-back work), the same settling every other measurement here gets
+    spin(step)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -473,18 +505,21 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     flops = prefill_flops(B, Hq, S, D, True)
     tflops = flops / (ms * 1e-3) / 1e12
-    # the step's attention kernel alone: the same launch (global configuration
-    # 0) with the workspace already holding the rotated K, so the rotation
-    # kernel is skipped; HIP events on the same stream.  The rest of the step
-    # is the K rotation and its launch.
+    # the step's attention kernel alone: the same launch (global configuration)
+    # with the workspace already holding the rotated K, so the rotation kernel
+    # is skipped; HIP events on the same stream (torch's current stream, which
+    # the binding passes to the library)
     ms_kern = time_loop(lambda: attn.prefill_gqa_rope(q, k, v, scale, causal=True, rope_theta=10000.0, out=out,
-                                                      workspace=ws, config=0 if cfg is None else cfg,
+                                                      workspace=ws, config=GLOBAL_CONFIG if cfg is None else cfg,
                                                       k_rotated=True),
-                        args.steps, args.warmup)
-    ms_pre = ms - ms_kern
+                        max(args.steps, 50), args.warmup)
+    # the step's K rotation alone: the same launch (attn_rope_rotate of K into
+    # the workspace), timed as its own loop
+    ws_k = ws.view(torch.bfloat16).view(k.shape)
+    ms_rot = time_loop(lambda: attn.rope_rotate(k, 10000.0, out=ws_k), max(args.steps, 50), args.warmup)
     kern_tflops = flops / (ms_kern * 1e-3) / 1e12
-    log(f"prefill gqa+rope bf16 S=2048: {ms * 1e3:.1f} us/step ({ms_pre * 1e3:.1f} us K rotation + "
-        f"{ms_kern * 1e3:.1f} us attention kernel), {tflops:.1f} TFLOP/s per step, "
+    log(f"prefill gqa+rope bf16 S=2048: {ms * 1e3:.1f} us/step; K rotation alone {ms_rot * 1e3:.1f} us, "
+        f"attention kernel alone {ms_kern * 1e3:.1f} us; {tflops:.1f} TFLOP/s per step, "
         f"{kern_tflops:.1f} TFLOP/s attention kernel")
 
     result = {
@@ -498,9 +533,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": prefill_traffic(),
-                     "kernel": "prefill_fwd_kernel<bf16,128,causal,RoPE on Q (K rotated once),4 waves>"
+                     "kernel": "prefill_sp_kernel<bf16,128,causal,RoPE on Q (K rotated once),4 waves>"
                                if cfg is None else f"prefill configuration {cfg}",
-                     "kernel_us": round(ms_kern * 1e3, 2), "k_rotation_us": round(ms_pre * 1e3, 2),
+                     "kernel_us": round(ms_kern * 1e3, 2), "k_rotation_us": round(ms_rot * 1e3, 2),
                      "algorithmic_per_launch": flops},
     }
 
@@ -517,7 +552,7 @@ def main():
         # MHA forward Z=4, H=32, fp16 and fp8 e5m2 (fp16 out)
         mha = {}
         for D_, causal in ((64, False), (128, True)):
-            for N in (1024, 4096, 16384):
+            for N in (1024, 2048, 4096, 8192, 16384):
                 for dt in ("f16", "fp8_e5m2"):
                     qm, km, vm = [t.to(dev) for t in prefill_inputs(4, 32, 32, N, D_, dt, seed=N)]
                     om = torch.empty(qm.shape, dtype=torch.float16, device=dev)

@@ -90,15 +90,15 @@ def test_prefill_k_rotated_flag_needs_workspace(lib):
                                                  None, 0, None)
     assert code == 5
     code = lib.attn_prefill_gqa_rope_with_config(P, P, P, P2, None, 1, 4, 2, 16, 64, _lib.ATTN_BF16, _lib.ATTN_BF16,
-                                                 0.125, 1, 10000.0, 1.0, 1.0, 1.0, _lib.ATTN_CONFIG_K_ROTATED | 7,
+                                                 0.125, 1, 10000.0, 1.0, 1.0, 1.0, _lib.ATTN_CONFIG_K_ROTATED | 9,
                                                  P, 1 << 20, None)
-    assert code == 6  # configuration 7 does not exist
+    assert code == 6  # configuration 9 does not exist
 
 
 def test_prefill_config_ids(lib):
-    # ids 0..6 are the sweep configurations (0 the global one); anything else is rejected on the host
-    assert lib.attn_prefill_num_configs() == 7
-    for bad in (-1, 7, 1000):
+    # ids 0..8 are the sweep configurations (7 the global one); anything else is rejected on the host
+    assert lib.attn_prefill_num_configs() == 9
+    for bad in (-1, 9, 1000):
         code = lib.attn_prefill_gqa_rope_with_config(P, P, P, P2, None, 1, 4, 2, 16, 64, _lib.ATTN_BF16,
                                                      _lib.ATTN_BF16, 0.125, 1, 0.0, 1.0, 1.0, 1.0, bad, None, 0, None)
         assert code == 6
@@ -150,6 +150,9 @@ def test_decode_gqa_rejects(lib):
     assert _gqa(lib, ws_bytes=1024) == 5
     assert _gqa(lib, ws=P + 16) == 4
     assert _gqa(lib, o=ODD) == 4
+    # the score scale must be positive and finite (as for the prefill)
+    for bad in (0.0, -0.1, float("nan"), float("inf"), float("-inf")):
+        assert _gqa(lib, scale=bad) == 2
 
 
 def test_decode_gqa_workspace_size(lib):
@@ -197,6 +200,8 @@ def test_decode_mla_rejects(lib):
     assert _mla(lib, split=48) == 2
     assert _mla(lib, ws_bytes=16) == 5
     assert _mla(lib, c=ODD) == 4
+    for bad in (0.0, -0.07, float("nan"), float("inf")):
+        assert _mla(lib, scale=bad) == 2
     # the split index is the second grid dimension: at most 65535 splits
     assert _mla(lib, B=1, cap=32 * 65536, split=32) == 2
 

@@ -100,7 +100,7 @@ def test_prefill_small_full(attn, dtype, D, causal, rope, B, Hq, Hkv, S, k_rope)
     assert _maxerr(lse, want_lse) <= 2e-2
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (4, 2)])
 @pytest.mark.parametrize("D,causal,rope,dtype", [(128, True, True, "bf16"), (64, False, False, "f16"),
                                                   (128, False, True, "f16"), (64, True, True, "bf16")])
@@ -109,7 +109,7 @@ def test_prefill_every_tile_config(attn, config, Hq, Hkv, D, causal, rope, dtype
     """Every tile configuration of the sweep passes parity before it is timed
     (GQA groups of 4, 1 and 2 query heads: different row layouts per wave),
     in both RoPE forms (K rotated once into the workspace, or per staged tile)."""
-    assert attn.prefill_num_configs() == 7
+    assert attn.prefill_num_configs() == 9
     if k_rope == "per_tile" and not rope:
         pytest.skip("no RoPE: both forms are the same launch")
     q, k, v = prefill_inputs(2, Hq, Hkv, 333, D, dtype, seed=config * 7 + D + Hq)
@@ -173,25 +173,52 @@ def test_prefill_tile_counts(attn, S, D, causal, rope, Hq, Hkv):
     assert _maxerr(lse, want_lse) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("config", [7, 8])
+@pytest.mark.parametrize("S", [1, 40, 64, 65, 128, 129, 192, 257, 320, 448, 449, 512, 577])
+@pytest.mark.parametrize("D,causal,rope,Hq,Hkv,dtype", [(128, True, True, 8, 2, "bf16"), (64, False, False, 4, 4, "f16"),
+                                                        (128, False, False, 4, 1, "bf16"), (64, True, True, 8, 8, "bf16"),
+                                                        (128, True, False, 12, 3, "f16")])
+def test_prefill_pipelined_tile_counts(attn, config, S, D, causal, rope, Hq, Hkv, dtype):
+    """The software-pipelined kernel (configurations 7 and 8) unrolls its key
+    loop over its LDS stages and keeps K and V tiles ahead in them; with 8
+    waves the halves take alternate key tiles and merge at the end (a half
+    may see no key of a row).  Sequences of 1 to 10 key tiles, full and
+    ragged, end the loop in every stage phase and leave either half short;
+    GQA groups of 4, 1 and 2 heads (and MHA) give the three wave layouts,
+    whose causal bounds differ per wave when the group is smaller than 4.
+    Every element and the LSE against the oracle."""
+    q, k, v = prefill_inputs(1, Hq, Hkv, S, D, dtype, seed=S + 3 * D)
+    theta = 10000.0 if rope else 0.0
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, rope_theta=theta,
+                                   return_lse=True, config=config)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, theta,
+                                    return_lse=True)
+    assert _maxerr(o, want) <= TOL[dtype]
+    assert _maxerr(lse, want_lse) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,S,D,dtype,causal,theta", [(4, 32, 32, 4096, 128, "f16", True, 0.0),
                                                             (2, 32, 8, 3000, 128, "bf16", True, 10000.0),
                                                             (4, 16, 16, 4096, 64, "f16", False, 0.0),
                                                             (1, 32, 8, 2048, 128, "bf16", True, 10000.0)])
 def test_prefill_persistent_equals_default(attn, B, Hq, Hkv, S, D, dtype, causal, theta):
     """Persistent scheduling (configuration 3) runs the per-item code of
-    configuration 0 (the global default) and only changes which workgroup takes
-    which item: the first three shapes have more than two residency rounds of
-    items, so every resident workgroup loops over several; the last (the
-    causal GQA RoPE prefill workload, 512 items) launches one workgroup per
-    item.  Outputs and LSEs are bit for bit equal in all of them."""
+    configuration 0 and only changes which workgroup takes which item: the
+    first three shapes have more than two residency rounds of items, so every
+    resident workgroup loops over several; the last (the causal GQA RoPE
+    prefill workload, 512 items) launches one workgroup per item.  Outputs and
+    LSEs are bit for bit equal; and the call without a configuration is the
+    global default, configuration 7, bit for bit."""
     q, k, v = _dev(*prefill_inputs(B, Hq, Hkv, S, D, dtype, seed=S + D))
     o0, l0 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta, config=0,
                                    return_lse=True)
     o3, l3 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta, config=3,
                                    return_lse=True)
     od, ld = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta, return_lse=True)
+    o7, l7 = attn.prefill_gqa_rope(q, k, v, 1 / math.sqrt(D), causal=causal, rope_theta=theta, config=7,
+                                   return_lse=True)
     assert torch.equal(o0, o3) and torch.equal(l0, l3)
-    assert torch.equal(od, o0) and torch.equal(ld, l0)
+    assert torch.equal(od, o7) and torch.equal(ld, l7)
 
 
 def test_prefill_k_rotated_flag_reuses_workspace(attn):
@@ -250,6 +277,31 @@ def test_prefill_out_dtype_f32_and_G8(attn):
     assert _maxerr(o, want) <= 2e-2
 
 
+def test_gqa_rope_full_size_every_element(attn):
+    """The causal GQA RoPE prefill workload at full size (B=1, Hq=32, Hkv=8,
+    S=2048, D=128, bf16, theta 10000), in the launch the benchmark times (K
+    rotated once into a workspace, the global configuration): every element
+    of O and every LSE against the oracle, one KV group (4 query heads) at a
+    time."""
+    q, k, v = prefill_inputs(1, 32, 8, 2048, 128, "bf16")
+    scale = 1 / math.sqrt(128)
+    ws = torch.empty(attn.prefill_gqa_rope_workspace_bytes(1, 8, 2048, 128, torch.bfloat16, 10000.0),
+                     dtype=torch.uint8, device="cuda")
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=True, rope_theta=10000.0, workspace=ws,
+                                   return_lse=True)
+    o, lse = o.cpu(), lse.cpu()
+    qd, kd, vd = to_f64(q), to_f64(k), to_f64(v)
+    worst = worst_lse = 0.0
+    for g in range(8):
+        want, want_lse = oracle.prefill(qd[:, 4 * g:4 * g + 4], kd[:, g:g + 1], vd[:, g:g + 1], scale, True, 10000.0,
+                                        return_lse=True)
+        worst = max(worst, _maxerr(o[:, 4 * g:4 * g + 4], want))
+        worst_lse = max(worst_lse, _maxerr(lse[:, 4 * g:4 * g + 4], want_lse))
+    print(f"causal GQA RoPE prefill, full size, every element: max-abs err {worst:.4g}, LSE {worst_lse:.4g}")
+    assert worst <= TOL["bf16"]
+    assert worst_lse <= TOL["bf16"]
+
+
 def test_gqa_rope_full_size_sampled(attn):
     """Causal GQA prefill with fused RoPE at full size: B=1, Hq=32, Hkv=8,
     S=2048, D=128, bf16, theta 10000; sampled rows of every head."""
@@ -266,13 +318,15 @@ def test_gqa_rope_full_size_sampled(attn):
     assert torch.isfinite(o.float()).all()
 
 
-@pytest.mark.parametrize("dtype,config", [("f16", 0), ("fp8_e5m2", 0), ("fp8_e5m2", 1)])
+@pytest.mark.parametrize("dtype,config", [("f16", None), ("f16", 0), ("fp8_e5m2", 0), ("fp8_e5m2", 1)])
 @pytest.mark.parametrize("D,causal", [(64, False), (128, True)])
-@pytest.mark.parametrize("N", [1024, 4096, 16384])
+@pytest.mark.parametrize("N", [1024, 2048, 4096, 8192, 16384])
 def test_mha_forward_sampled(attn, dtype, config, D, causal, N):
-    """MHA forward Z=4, H=32 (fp16 or fp8 e5m2 in, fp16 out): sampled rows of
-    sampled heads, including (0, 0) and (3, 31); fp8 with P in e4m3 on the
-    fp8 MFMA (configuration 0) and in f16 (configuration 1)."""
+    """MHA forward Z=4, H=32 (fp16 or fp8 e5m2 in, fp16 out) at every N_CTX of
+    the sweep: sampled rows of sampled heads, including (0, 0) and (3, 31);
+    fp16 in the global configuration and in configuration 0, fp8 with P in
+    e4m3 on the fp8 MFMA (configuration 0, its default) and in f16
+    (configuration 1).  The worst error is printed for the record."""
     q, k, v = prefill_inputs(4, 32, 32, N, D, dtype, seed=N + D)
     scale = 1 / math.sqrt(D)
     o = attn.prefill_gqa_rope(*_dev(q, k, v), scale, causal=causal, out_dtype=torch.float16, config=config).cpu()
@@ -284,6 +338,7 @@ def test_mha_forward_sampled(attn, dtype, config, D, causal, N):
     for z, h in heads:
         want, _ = oracle.prefill_rows(qn, kn, vn, scale, causal, 0.0, z, h, rows)
         worst = max(worst, _maxerr(o[z, h, rows], want))
+    print(f"mha {dtype} config {config} D{D} {'causal' if causal else 'non-causal'} N{N}: max-abs err {worst:.4g}")
     assert worst <= TOL[dtype]
 
 
@@ -364,7 +419,8 @@ def test_prefill_unfused_matches_oracle(attn, D, Hq, Hkv, S):
 # ----------------------------------------------------------------------------
 # GQA decode
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("B,split", [(1, 128), (8, 128), (128, 128), (1, 0), (128, 0), (8, 1024), (128, 1024)])
+@pytest.mark.parametrize("B,split", [(1, 128), (8, 128), (128, 128), (1, 0), (8, 0), (32, 0), (64, 0), (128, 0),
+                                     (32, 128), (64, 1024), (8, 1024), (128, 1024)])
 def test_decode_gqa_config(attn, B, split):
     """GQA decode: Hq=16, Hkv=4, D=128, context 2048 in capacity 2056, at most
     128 slots per wave (the decode audit's split size and the library default

@@ -129,6 +129,29 @@ def test_softmax_rows_sum_to_one_and_shift_invariance():
     assert np.max(np.abs(o - 1.0)) <= 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_probs_match_brute_force(causal):
+    """attention_probs against the pure-Python brute force: attending to
+    one-hot value rows (value j = e_j) returns the probability row itself, so
+    brute.attend over the visible keys gives row i of the probabilities
+    (zeros past the causal bound).  A doubled or dropped scale fails this."""
+    rng = np.random.default_rng(11)
+    S, D, scale = 9, 6, 0.37
+    q, k = rng.standard_normal((S, D)), rng.standard_normal((S, D))
+    p = oracle.attention_probs(q, k, scale, causal)
+    for i in range(S):
+        n = i + 1 if causal else S
+        eye = [[1.0 if c == j else 0.0 for c in range(n)] for j in range(n)]
+        want = brute.attend(list(q[i]), [list(r) for r in k[:n]], eye, scale) + [0.0] * (S - n)
+        assert np.max(np.abs(p[i] - np.asarray(want))) <= 1e-12
+    # sampled rows: the same probabilities by row index
+    rows = [0, 4, 8]
+    assert np.max(np.abs(oracle.attention_probs(q[rows], k, scale, causal, rows=rows) - p[rows])) <= 1e-15
+    # a planted doubled scale is caught
+    bad = oracle.attention_probs(q, k, 2 * scale, causal)
+    assert np.max(np.abs(bad - p)) > 1e-3
+
+
 def test_causal_invariance():
     rng = np.random.default_rng(2)
     B, Hq, Hkv, S, D = 1, 4, 2, 24, 8
