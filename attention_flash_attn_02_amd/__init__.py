@@ -1,8 +1,8 @@
 """MI355X (gfx950) attention forward: HIP kernels behind a C ABI (include/attn.h).
 
 Python entry points (same names as the C calls, without the ``attn_`` prefix):
-prefill_gqa_rope, rope_rotate, decode_gqa, decode_mla, combine_splits,
-kv_append, prefill_chunk, and the workspace size queries;
+prefill_gqa_rope, rope_rotate, decode_gqa, decode_gqa_noalloc, decode_mla,
+combine_splits, kv_append, prefill_chunk, and the workspace size queries;
 prefill_gqa_rope_unfused composes rope_rotate with the attention call.
 libattn.so is loaded on first use; every call raises ImportError if it has
 not been built (there is no other code path).
@@ -11,6 +11,7 @@ from ._lib import AttnError, lib  # noqa: F401
 from .ops import (  # noqa: F401
     combine_splits,
     decode_gqa,
+    decode_gqa_noalloc,
     decode_gqa_workspace_bytes,
     decode_mla,
     decode_mla_workspace_bytes,

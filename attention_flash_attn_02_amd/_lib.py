@@ -39,6 +39,8 @@ SIGNATURES = {
     "attn_decode_gqa_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_decode_gqa": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _c_int, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _c_int, _c_float, _vp]),
+    "attn_decode_gqa_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _c_int, _c_int, _c_float, _vp]),
     "attn_decode_mla_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_decode_mla": (_c_int, [_vp, _vp, _vp, _vp, _vp, _sz, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _c_float, _vp]),

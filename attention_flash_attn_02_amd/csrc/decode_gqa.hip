@@ -15,6 +15,8 @@
 // written directly and a decode step is one kernel.  Slots at or past kv_len are never loaded; a wave or workgroup
 // without slots contributes the empty part (o = 0, lse = -inf).
 
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -339,4 +341,49 @@ extern "C" attn_status attn_decode_gqa(const void* q, const void* k_cache, const
   if (st != ATTN_OK || n_wg == 1) return st;
   launch_combine(p.o_part, p.lse_part, o, B * Hq, n_wg, D, dtype, stream);
   return attn_host::launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free form: the split partials go to a file-scope device array
+// instead of a caller workspace.  The array's name is only a host-side
+// stand-in for the symbol; its device address (one per GPU) comes from
+// hipGetSymbolAddress on the first call on that GPU, and only that address
+// is passed to the kernels.  Every call on a GPU shares its array, so calls
+// that overlap on one GPU (two streams, two threads) race.  Nothing in it
+// needs clearing: the split kernel writes every part slot (empty ranges as
+// o = 0, lse = -inf) before the combine kernel reads it.
+// ---------------------------------------------------------------------------
+static constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;  // 8 MiB per GPU
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+
+// device address of this GPU's scratch (the current device), or null
+static void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+extern "C" attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                               const int32_t* kv_len, void* o, int B, int Hq, int Hkv, int D,
+                                               int cap, int split, attn_dtype dtype, float softmax_scale,
+                                               hipStream_t stream) {
+  const size_t need = attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split);
+  if (need > kNoAllocScratchBytes) return ATTN_ERR_WORKSPACE;  // beyond the static scratch
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address();
+    if (!ws) return ATTN_ERR_LAUNCH;
+  }
+  return attn_decode_gqa(q, k_cache, v_cache, kv_len, o, ws, need, B, Hq, Hkv, D, cap, split, dtype,
+                         softmax_scale, stream);
 }

@@ -265,6 +265,29 @@ def decode_gqa(q, k_cache, v_cache, kv_len, softmax_scale: float, split: int = 0
     return out
 
 
+def decode_gqa_noalloc(q, k_cache, v_cache, kv_len, softmax_scale: float, split: int = 0, out=None, stream=None):
+    """attn_decode_gqa_noalloc: decode_gqa with the split partials in the
+    library's static device scratch (no workspace, no device allocation when
+    ``out`` is given).  Calls that overlap on one GPU race on that scratch."""
+    _ndim(q, "q", 3)
+    _ndim(k_cache, "k_cache", 4)
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    _shape(k_cache, "k_cache", (B, Hkv, cap, D), q.dtype)
+    _shape(v_cache, "v_cache", (B, Hkv, cap, D), q.dtype)
+    _shape(kv_len, "kv_len", (B,), torch.int32)
+    if out is not None:
+        _shape(out, "out", (B, Hq, D), q.dtype)
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, kv_len=kv_len, out=out)
+    if out is None:
+        out = torch.empty_like(q)
+    code = _lib.lib().attn_decode_gqa_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(kv_len, "kv_len"),
+        _dev(out, "out"), B, Hq, Hkv, D, cap, int(split), _dtype_code(q), float(softmax_scale), _stream(stream))
+    _lib.check(code)
+    return out
+
+
 def decode_mla_workspace_bytes(B, H, cap, d_latent, split=0) -> int:
     return int(_lib.lib().attn_decode_mla_workspace_bytes(B, H, cap, d_latent, split))
 

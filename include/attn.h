@@ -218,6 +218,29 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
                             hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * attn_decode_gqa without a workspace, for callers that cannot allocate
+ * device memory (code under stream capture that must not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation).  The same
+ * operation, arguments, kernels and error checks as attn_decode_gqa; the
+ * split partials go to a static device array of the library (8 MiB per GPU,
+ * kept until the process ends) instead of a caller workspace.
+ *   Limit: attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split) must not
+ *   exceed 8 MiB (8388608 bytes), else ATTN_ERR_WORKSPACE and nothing is
+ *   launched.  The default split at capacity 2056 (five partial parts of
+ *   128 floats per query row) fits up to B * Hq = 3276 rows.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (different streams or host threads) race and must be ordered by the
+ *   caller.  The array needs no clearing between calls.
+ *   The first call on a GPU looks up the array's address there
+ *   (hipGetSymbolAddress; ATTN_ERR_LAUNCH if that fails).  No call
+ *   allocates or frees memory.
+ * ------------------------------------------------------------------------ */
+attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* kv_len, void* o, int B, int Hq, int Hkv, int D,
+                                    int cap, int split, attn_dtype dtype, float softmax_scale,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Absorbed-MLA decode: H query heads share one latent cache row per token.
  *
  *   q        [B, H, d_latent + d_rope]    dtype, the absorbed query
