@@ -336,7 +336,7 @@ def sweep(scale):
         out["prefill_" + name] = {"us": times, "global": g, "best": min(times, key=times.get),
                                   "gap_pct": round(100 * (times[g] / best - 1), 2)}
         del q, k, v, o, ws
-    for kind, Bs, sc in (("gqa", (1, 8, 32, 64, 128), scale), ("mla", (1, 32, 128), 1 / math.sqrt(192))):
+    for kind, Bs, sc in (("gqa", (1, 8, 32, 64, 128), scale), ("mla", (1, 8, 32, 64, 128), 1 / math.sqrt(192))):
         for Bd in Bs:
             times = {}
             for sp in (0, 64, 128, 256, 512, 1024):
@@ -376,7 +376,8 @@ def prefill_traffic():
         return None
 
 
-PREFILL_SOURCES = ("attention_flash_attn_02_amd/csrc/prefill.hip", "attention_flash_attn_02_amd/csrc/common.hpp")
+PREFILL_SOURCES = ("attention_flash_attn_02_amd/csrc/prefill.hip", "attention_flash_attn_02_amd/csrc/prefill_sp.hip",
+                   "attention_flash_attn_02_amd/csrc/prefill_common.hpp", "attention_flash_attn_02_amd/csrc/common.hpp")
 
 
 def cpu_baseline(budget_s=15.0):

@@ -10,7 +10,9 @@
  *  - All tensor pointers are DEVICE pointers to contiguous row-major arrays
  *    with the head dimension innermost.  The caller owns every buffer,
  *    including the workspace; the library allocates and frees nothing and
- *    keeps no mutable global state, so calls are thread-safe.
+ *    keeps no mutable global state, so calls are thread-safe.  The one
+ *    exception is attn_decode_gqa_noalloc, whose partials live in a static
+ *    device array shared by all its calls on a GPU (see there).
  *  - Calls only enqueue kernels on `stream` and return; nothing synchronises
  *    with the host, so every call is legal inside hipGraph stream capture.
  *  - Host-side argument checks run before anything is launched; on a
@@ -186,7 +188,11 @@ attn_status attn_rope_rotate(const void* x, void* y, int B, int H, int S, int D,
 
 /* ------------------------------------------------------------------------ *
  * Split-context GQA decode ("flash-decoding"): one new query token per
- * sequence against a static KV cache.
+ * sequence against a static KV cache.  Defined by "Fixed-budget decode
+ * audit": section "Which implementation was tested" (a fused split-score
+ * kernel over a static append cache), section "Setup and interpretation"
+ * (BF16, context 2048 in a cache of capacity 2056, batches 1 to 128) and
+ * section "Optimized full-model results" (split size 128, graph replay).
  *
  *   q        [B, Hq, D]        dtype
  *   k_cache  [B, Hkv, cap, D]  dtype (slot t holds the key of position t)
@@ -242,6 +248,10 @@ attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const vo
 
 /* ------------------------------------------------------------------------ *
  * Absorbed-MLA decode: H query heads share one latent cache row per token.
+ * Defined by "Fixed-budget decode audit": section "Which implementation was
+ * tested" (MLA with absorption, a 448-d latent plus a 64-d RoPE part per
+ * token) and section "Like-for-like eager absorption comparison" (the
+ * "MLA absorbed" row at batch 128, context 2048).
  *
  *   q        [B, H, d_latent + d_rope]    dtype, the absorbed query
  *            [W_UK q_nope ; q_rope] (latent part first)
@@ -252,8 +262,11 @@ attn_status attn_decode_gqa_noalloc(const void* q, const void* k_cache, const vo
  *
  * Scores use all d_latent + d_rope dims; values are the latent part of the
  * same rows.  dtype: ATTN_BF16 or ATTN_F16.  d_latent = 448, d_rope = 64,
- * H <= 16.  split <= 0 picks the library default (256); otherwise a multiple
- * of 32 in [32, 2048], with ceil(cap / split) <= 65535 (else ATTN_ERR_SHAPE).
+ * H <= 16.  split <= 0 (the default) cuts [0, kv_len[b]) on the device into
+ * n equal runs of 32-slot chunks, n = round(compute units / B) clamped to
+ * [1, min(16, ceil(cap / 32))], so one setting serves batch 1 and batch 128;
+ * otherwise split is a fixed run length in slots, a multiple of 32 in
+ * [32, 2048], with ceil(cap / split) <= 65535 (else ATTN_ERR_SHAPE).
  * Launches two kernels on `stream`.
  * ------------------------------------------------------------------------ */
 size_t attn_decode_mla_workspace_bytes(int B, int H, int cap, int d_latent, int split);
@@ -263,7 +276,12 @@ attn_status attn_decode_mla(const void* q, const void* kv_cache, const int32_t* 
                             float softmax_scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
- * Split-softmax combine (the merge of softmax parts): for each of R rows,
+ * Split-softmax combine (the merge of softmax parts).  Defined by
+ * "Fixed-budget decode audit", section "A: group-entry queries and one
+ * joint history scan" (an output and its log-sum-exp merged with a second
+ * part through a sigmoid of the log-sum-exp difference), generalised to
+ * many parts; section "Measured group-attention times" names the split
+ * reduction this step performs.  For each of R rows,
  *   o[r] = sum_s w_s o_part[r, s] / sum_s w_s,  w_s = exp(lse_part[r, s] - max_s lse_part[r, s]).
  * This equals folding the pairwise merge alpha = sigmoid(lse_b - lse_a),
  * o = (1 - alpha) o_a + alpha o_b over the parts.  A part with

@@ -541,9 +541,11 @@ def test_decode_workspace_reuse(attn):
 @pytest.mark.parametrize("split", [0, 1024])
 def test_decode_mla_hipgraph_replay(attn, split):
     """MLA decode (split kernel + combine of bf16 parts) captured in a hipGraph
-    replays bit-equal to the eager call; the default split leaves the ninth
-    split of the 2056-slot capacity empty.  A shorter length set in device
-    memory takes effect without re-capture."""
+    replays bit-equal to the eager call: the default work division (equal
+    runs of 32-slot chunks of [0, kv_len), divided on the device) and a fixed
+    split of 1024 whose third part (slots 2048..2055) is empty.  A shorter
+    length set in device memory takes effect without re-capture (with the
+    default division, 22 chunks over more parts: some parts empty)."""
     q, c, L = _dev(*decode_mla_inputs(8, 16, 448, 64, 2056, 2048, "bf16", seed=4))
     ws = torch.empty(attn.decode_mla_workspace_bytes(8, 16, 2056, 448, split), dtype=torch.uint8, device="cuda")
     out = torch.empty((8, 16, 448), dtype=torch.bfloat16, device="cuda")
@@ -571,18 +573,23 @@ def test_decode_mla_hipgraph_replay(attn, split):
     assert _maxerr(out, want) <= 2e-2
 
 
-@pytest.mark.parametrize("B", [1, 32, 128])
-def test_decode_mla_config(attn, B):
+@pytest.mark.parametrize("B", [1, 8, 32, 64, 128])
+@pytest.mark.parametrize("split", [0, 256, 1024])
+def test_decode_mla_config(attn, B, split):
     """Absorbed-MLA decode: H=16, latent 448 + rope 64, context 2048 in
-    capacity 2056, scale 1/sqrt(192), bf16; NaN in the unused slots."""
+    capacity 2056, scale 1/sqrt(192), bf16; NaN in the unused slots.  The
+    default work division (split 0: parts per sequence chosen from the batch)
+    and fixed splits; the worst error is printed for the record."""
     q, c, L = decode_mla_inputs(B, 16, 448, 64, 2056, 2048, "bf16", nan_tail=True)
     scale = 1 / math.sqrt(192)
-    o = attn.decode_mla(*_dev(q, c, L), scale)
+    o = attn.decode_mla(*_dev(q, c, L), scale, split=split)
     want = oracle.decode_mla(to_f64(q), to_f64(c), L.numpy(), scale, 448)
-    assert _maxerr(o, want) <= 2e-2
+    err = _maxerr(o, want)
+    print(f"mla decode B{B} split {split}: max-abs err {err:.4g}")
+    assert err <= 2e-2
 
 
-@pytest.mark.parametrize("split", [32, 128, 256, 512, 2048])
+@pytest.mark.parametrize("split", [0, 32, 128, 256, 512, 2048])
 def test_decode_mla_ragged(attn, split):
     lengths = [0, 1, 33, 256, 257, 2056]
     q, c, L = decode_mla_inputs(len(lengths), 16, 448, 64, 2056, 0, "bf16", seed=split, nan_tail=True,
