@@ -31,7 +31,8 @@ COMMON_FLAGS = [
 # per-source flags.  prefill_sp.hip: select the VGPR form of the MFMAs, so
 # the score tiles the softmax reads stay in VGPRs (with accumulation
 # registers the compiler keeps copying them back and forth).
-SOURCE_FLAGS = {"prefill_sp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+SOURCE_FLAGS = {"prefill_sp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "prefill_sp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd):

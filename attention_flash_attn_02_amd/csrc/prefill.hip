@@ -1849,6 +1849,10 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
     launch_prefill_sp(p, in_dtype == ATTN_BF16, c, rope_mode == 2, config == 8 ? 2 : 1, stream);
     return attn_host::launch_status();
   }
+  if ((config == 7 || config == 8) && in_dtype == ATTN_FP8_E5M2) {
+    launch_prefill_sp8(p, c, stream);
+    return attn_host::launch_status();
+  }
   if (config == 7 || config == 8) config = 0;
   switch (in_dtype) {
     case ATTN_BF16:

@@ -63,6 +63,8 @@ __device__ inline float pair_sum32(float x) {
 // software-pipelined 16-bit prefill kernel (one wave per SIMD), prefill_sp.hip
 // (halves 1: 4-wave workgroups; 2: 8-wave workgroups splitting the key tiles)
 void launch_prefill_sp(const PrefillParams& p, bool bf16, bool causal, bool rope_q, int halves, hipStream_t st);
+// software-pipelined fp8 e5m2 prefill kernel (P in e4m3), prefill_sp8.hip
+void launch_prefill_sp8(const PrefillParams& p, bool causal, hipStream_t st);
 
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 

@@ -440,11 +440,15 @@ def main():
     ap.add_argument("--prefill-config", type=int, default=None,
                     help="profiling runs only (with --quick): run the prefill step in this sweep "
                          "configuration instead of the global one")
+    ap.add_argument("--mha-only", default=None, metavar="DTYPE,D,N",
+                    help="profiling runs: time only the Z=4, H=32 MHA forward of this dtype (f16 or "
+                         "fp8_e5m2), head dim (64: non-causal, 128: causal) and length, `steps` calls "
+                         "after `warmup`; prints one JSON line of its own")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
-    if args.prefill_config is not None and not args.quick:
-        log("--prefill-config is for profiling runs and needs --quick")
+    if args.prefill_config is not None and not (args.quick or args.mha_only):
+        log("--prefill-config is for profiling runs and needs --quick or --mha-only")
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -466,6 +470,22 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    if args.mha_only:
+        dt, D_, N = args.mha_only.split(",")
+        D_, N = int(D_), int(N)
+        causal = D_ == 128
+        qm, km, vm = [t.to(dev) for t in prefill_inputs(4, 32, 32, N, D_, dt, seed=N)]
+        om = torch.empty(qm.shape, dtype=torch.float16, device=dev)
+        cfg = args.prefill_config
+        ms_m = time_loop(lambda: attn.prefill_gqa_rope(qm, km, vm, 1 / math.sqrt(D_), causal=causal, out=om,
+                                                      config=cfg), args.steps, args.warmup)
+        tf = prefill_flops(4, 32, N, D_, causal) / (ms_m * 1e-3) / 1e12
+        peak = PEAK_FP8_TFLOPS if dt.startswith("fp8") else PEAK_BF16_TFLOPS
+        print(json.dumps({"mha_only": {"dtype": dt, "D": D_, "N": N, "causal": causal, "config": cfg,
+                                       "us": round(ms_m * 1e3, 2), "tflops": round(tf, 1),
+                                       "frac": round(tf / peak, 4)}}), flush=True)
+        return
 
     if args.decode_only:
         out = {}
@@ -514,12 +534,19 @@ def main():
                                                       workspace=ws, config=GLOBAL_CONFIG if cfg is None else cfg,
                                                       k_rotated=True),
                         max(args.steps, 50), args.warmup)
-    # the step's K rotation alone: the same launch (attn_rope_rotate of K into
-    # the workspace), timed as its own loop
+    # the K rotation's share of the step: step time minus the attention kernel
+    # alone (the rotation kernel plus the one launch gap it adds; inside the
+    # step K arrives cold, after the attention kernel has used the caches)
+    ms_rot = ms - ms_kern
+    # the same rotation launch on its own (attn_rope_rotate of K into the
+    # workspace), 20 launches per captured graph so that the host's per-call
+    # overhead is not what is timed; back to back, K stays cache-resident and
+    # the time includes one dispatch gap per launch
     ws_k = ws.view(torch.bfloat16).view(k.shape)
-    ms_rot = time_loop(lambda: attn.rope_rotate(k, 10000.0, out=ws_k), max(args.steps, 50), args.warmup)
+    ms_rot_alone = time_graph(lambda: attn.rope_rotate(k, 10000.0, out=ws_k), 20, max(args.steps // 10, 10))
     kern_tflops = flops / (ms_kern * 1e-3) / 1e12
-    log(f"prefill gqa+rope bf16 S=2048: {ms * 1e3:.1f} us/step; K rotation alone {ms_rot * 1e3:.1f} us, "
+    log(f"prefill gqa+rope bf16 S=2048: {ms * 1e3:.1f} us/step; K rotation {ms_rot * 1e3:.1f} us of it "
+        f"({ms_rot_alone * 1e3:.1f} us alone in a graph), "
         f"attention kernel alone {ms_kern * 1e3:.1f} us; {tflops:.1f} TFLOP/s per step, "
         f"{kern_tflops:.1f} TFLOP/s attention kernel")
 
@@ -537,6 +564,7 @@ def main():
                      "kernel": "prefill_sp_kernel<bf16,128,causal,RoPE on Q (K rotated once),4 waves>"
                                if cfg is None else f"prefill configuration {cfg}",
                      "kernel_us": round(ms_kern * 1e3, 2), "k_rotation_us": round(ms_rot * 1e3, 2),
+                     "k_rotation_alone_graph_us": round(ms_rot_alone * 1e3, 2),
                      "algorithmic_per_launch": flops},
     }
 
@@ -577,7 +605,7 @@ def main():
             log(f"decode gqa B={Bd}:", json.dumps(gqa[f"B{Bd}"]))
         sec["decode_gqa"] = gqa
         mla = {}
-        for Bd in (1, 32, 128):
+        for Bd in (1, 8, 32, 64, 128):
             mla[f"B{Bd}"] = decode_case("mla", Bd, 0, 1 / math.sqrt(192))
             log(f"decode mla B={Bd}:", json.dumps(mla[f"B{Bd}"]))
         sec["decode_mla"] = mla

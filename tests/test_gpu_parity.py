@@ -197,6 +197,43 @@ def test_prefill_pipelined_tile_counts(attn, config, S, D, causal, rope, Hq, Hkv
     assert _maxerr(lse, want_lse) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("config", [7, 8])
+@pytest.mark.parametrize("S", [1, 40, 64, 65, 128, 129, 192, 257, 320, 448, 449, 512, 577])
+@pytest.mark.parametrize("D,causal,Hq,Hkv", [(128, True, 8, 2), (64, False, 4, 4), (128, False, 4, 1),
+                                             (64, True, 8, 8), (128, True, 12, 3)])
+def test_prefill_fp8_pipelined_tile_counts(attn, config, S, D, causal, Hq, Hkv):
+    """The fp8 software-pipelined kernel (configurations 7 and 8 for fp8
+    e5m2 inputs): its key loop runs one iteration past the last tile (PV lags
+    the scores by a tile) and is unrolled over four LDS stages, so sequences
+    of 1 to 10 key tiles, full and ragged, end it in every stage phase; GQA
+    groups of 4, 1 and 2 heads give the three wave layouts.  Every element
+    and the LSE against the oracle."""
+    q, k, v = prefill_inputs(1, Hq, Hkv, S, D, "fp8_e5m2", seed=S + 5 * D)
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, out_dtype=torch.float32,
+                                   return_lse=True, config=config)
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, 0.0,
+                                    return_lse=True)
+    assert _maxerr(o, want) <= TOL["fp8_e5m2"]
+    assert _maxerr(lse, want_lse) <= TOL["fp8_e5m2"]
+
+
+def test_prefill_fp8_pipelined_large_scores(attn):
+    """Scores far above the first tile's maximum (the reference moves in
+    several later tiles, each move pending until the tile made with the old
+    reference is in O) and rows whose first tiles are all far below later
+    ones: every element and the LSE against the oracle."""
+    q, k, v = prefill_inputs(1, 4, 4, 700, 128, "fp8_e5m2", seed=21)
+    k = k.float()
+    ramp = torch.linspace(0.25, 6.0, 700).view(1, 1, 700, 1)  # keys grow along the sequence
+    k = (k * ramp).to(torch.float8_e5m2)
+    for causal in (True, False):
+        o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 0.5, causal=causal, out_dtype=torch.float32,
+                                       return_lse=True)
+        want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 0.5, causal, 0.0, return_lse=True)
+        assert _maxerr(o, want) <= TOL["fp8_e5m2"]
+        assert _maxerr(lse, want_lse) <= TOL["fp8_e5m2"]
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,S,D,dtype,causal,theta", [(4, 32, 32, 4096, 128, "f16", True, 0.0),
                                                             (2, 32, 8, 3000, 128, "bf16", True, 10000.0),
                                                             (4, 16, 16, 4096, 64, "f16", False, 0.0),
@@ -318,14 +355,16 @@ def test_gqa_rope_full_size_sampled(attn):
     assert torch.isfinite(o.float()).all()
 
 
-@pytest.mark.parametrize("dtype,config", [("f16", None), ("f16", 0), ("fp8_e5m2", 0), ("fp8_e5m2", 1)])
+@pytest.mark.parametrize("dtype,config", [("f16", None), ("f16", 0), ("fp8_e5m2", None), ("fp8_e5m2", 0),
+                                          ("fp8_e5m2", 1)])
 @pytest.mark.parametrize("D,causal", [(64, False), (128, True)])
 @pytest.mark.parametrize("N", [1024, 2048, 4096, 8192, 16384])
 def test_mha_forward_sampled(attn, dtype, config, D, causal, N):
     """MHA forward Z=4, H=32 (fp16 or fp8 e5m2 in, fp16 out) at every N_CTX of
     the sweep: sampled rows of sampled heads, including (0, 0) and (3, 31);
-    fp16 in the global configuration and in configuration 0, fp8 with P in
-    e4m3 on the fp8 MFMA (configuration 0, its default) and in f16
+    fp16 in the global configuration and in configuration 0, fp8 in the
+    global configuration (the pipelined fp8 kernel, P in e4m3), with P in
+    e4m3 in the 4-wave kernel (configuration 0) and with P in f16
     (configuration 1).  The worst error is printed for the record."""
     q, k, v = prefill_inputs(4, 32, 32, N, D, dtype, seed=N + D)
     scale = 1 / math.sqrt(D)
@@ -351,16 +390,18 @@ def test_mha_forward_full_small(attn):
         assert _maxerr(o, want) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("config", [0, 7])
 @pytest.mark.parametrize("D,causal", [(64, False), (128, True)])
-def test_fp8_e4m3_p_full(attn, D, causal):
-    """fp8 inputs with P rounded to e4m3 for the PV MFMA (the fp8 default,
+def test_fp8_e4m3_p_full(attn, D, causal, config):
+    """fp8 inputs with P rounded to e4m3 for the PV MFMA (the pipelined
+    kernel of the global configuration, and the 4-wave kernel of
     configuration 0): every element at N=1024 (with a ragged N=1000 too)
     within the fp8 tolerance; the row sums are those of the rounded
     probabilities."""
     for N in (1024, 1000):
         q, k, v = prefill_inputs(1, 8, 8, N, D, "fp8_e5m2", seed=N + D + 5)
         o = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, out_dtype=torch.float16,
-                                  config=0)
+                                  config=config)
         want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal)
         assert _maxerr(o, want) <= TOL["fp8_e5m2"]
 
