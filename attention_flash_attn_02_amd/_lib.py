@@ -50,7 +50,7 @@ SIGNATURES = {
                                 _c_int, _c_float, _c_int, _vp]),
     "attn_prefill_chunk_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _c_int, _c_int, _c_int, _c_int,
-                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp]),
+                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_float, _vp]),
 }
 
 

@@ -464,7 +464,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
 // CHUNK: the queries are a chunk of p.S rows at the end of a cache prefix:
 // K/V rows come from caches with p.cap slots per head, the key length of
 // sequence b is kv_len[b] (read on the device) and query row r sits at
-// position kv_len[b] - p.S + r (causal with that offset).
+// position kv_len[b] - p.S + r (causal with that offset).  With RoPE (mode
+// 2) the Q rows are rotated here to those positions; the cached K rows were
+// rotated when they were appended.
 // PERSIST: resident workgroups loop over several items (see below).
 // BNT: keys per tile.  64 by default; 32 halves the LDS of a workgroup
 // (three workgroups, i.e. three waves per SIMD, fit a compute unit) and the
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
 template <class Tag, int D, bool CAUSAL, int ROPE, int HALVES, bool CHUNK = false, bool PERSIST = false, int BNT = 64,
           bool PP = false, bool RS = false>
 __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_kernel(const PrefillParams p) {
-  static_assert(!CHUNK || (CAUSAL && !ROPE && HALVES == 1), "chunk mode: causal, no RoPE, 4 waves");
+  static_assert(!CHUNK || (CAUSAL && ROPE != 1 && HALVES == 1), "chunk mode: causal, K already rotated, 4 waves");
   static_assert(!PERSIST || (HALVES == 1 && !CHUNK), "persistent scheduling: 4 waves, plain prefill");
   static_assert(BNT == 64 || (BNT == 32 && ROPE != 1 && HALVES == 1 && !CHUNK && !PERSIST),
                 "32-key tiles: plain 4-wave kernel with K moved by DMA");
@@ -774,7 +776,8 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
             for (int s = 0; s < 2; ++s) {
               // angle in revolutions (v_sin/v_cos take revolutions)
               const int fi = 16 * kk + 8 * hh + 2 * e + s;
-              const float rev = __builtin_amdgcn_fractf((float)qpos * p.rope_fhi[fi]) + (float)qpos * p.rope_flo[fi];
+              const float pos = (float)(CHUNK ? max(qoff + qpos, 0) : qpos);
+              const float rev = __builtin_amdgcn_fractf(pos * p.rope_fhi[fi]) + pos * p.rope_flo[fi];
               const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
               const float x1 = Tag::to_f32(s ? (w1 >> 16) : (w1 & 0xffff));
               const float x2 = Tag::to_f32(s ? (w2 >> 16) : (w2 & 0xffff));
@@ -1977,11 +1980,18 @@ extern "C" size_t attn_prefill_chunk_workspace_bytes(int B, int Hq, int Hkv, int
   return split_workspace((long long)B * Hq * T, nsplit, D).total;
 }
 
+// chunk-mode launch: RoPE mode 2 (Q rotated in the kernel) or none
+template <class Tag, int D>
+static void launch_chunk_kernel(const PrefillParams& p, bool rope, dim3 grid, dim3 block, hipStream_t st) {
+  if (rope) hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, 2, 1, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, 0, 1, true>), grid, block, 0, st, p);
+}
+
 extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
                                           const int32_t* kv_len, void* o, float* lse, void* workspace,
                                           size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D,
                                           int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
-                                          float softmax_scale, hipStream_t stream) {
+                                          float softmax_scale, float rope_theta, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !kv_len || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || cap <= 0 || T > cap) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -1991,6 +2001,8 @@ extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, co
   if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!(softmax_scale > 0.f) || !(softmax_scale < 3.0e38f)) return ATTN_ERR_SHAPE;
+  if (rope_theta != rope_theta || !(rope_theta < 3.0e38f)) return ATTN_ERR_SHAPE;
+  if (rope_theta > 0.f && cap > 65536) return ATTN_ERR_UNSUPPORTED;  // exact angle reduction needs pos < 2^16
   if (!attn_host::aligned(q, 16) || !attn_host::aligned(k_cache, 16) || !attn_host::aligned(v_cache, 16) ||
       !attn_host::aligned(o, 16) || !attn_host::aligned(kv_len, 4) || (lse && !attn_host::aligned(lse, 4)))
     return ATTN_ERR_ALIGN;
@@ -2030,12 +2042,17 @@ extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, co
   const long long items = (long long)p.n_ptiles * B * Hkv * p.n_hgroups * nsplit;
   if (items > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   const dim3 grid((unsigned)items), block(256);
+  const bool rope = rope_theta > 0.f;
+  if (rope) {
+    p.rope = 2;
+    attn_host::rope_freq_split(rope_theta, D, p.inv_freq, p.rope_fhi, p.rope_flo);
+  }
   if (dtype == ATTN_BF16) {
-    if (D == 64) hipLaunchKernelGGL((prefill_fwd_kernel<Bf16Tag, 64, true, false, 1, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_fwd_kernel<Bf16Tag, 128, true, false, 1, true>), grid, block, 0, stream, p);
+    if (D == 64) launch_chunk_kernel<Bf16Tag, 64>(p, rope, grid, block, stream);
+    else launch_chunk_kernel<Bf16Tag, 128>(p, rope, grid, block, stream);
   } else {
-    if (D == 64) hipLaunchKernelGGL((prefill_fwd_kernel<F16Tag, 64, true, false, 1, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_fwd_kernel<F16Tag, 128, true, false, 1, true>), grid, block, 0, stream, p);
+    if (D == 64) launch_chunk_kernel<F16Tag, 64>(p, rope, grid, block, stream);
+    else launch_chunk_kernel<F16Tag, 128>(p, rope, grid, block, stream);
   }
   if (nsplit > 1) launch_combine(p.ws_o, p.ws_lse, o, (int)R, nsplit, D, out_dtype, stream, lse);
   return attn_host::launch_status();

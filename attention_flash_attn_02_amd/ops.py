@@ -204,11 +204,14 @@ def prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split=0) -> int:
 
 
 def prefill_chunk(q, k_cache, v_cache, kv_len, softmax_scale: float, out_dtype=None, out=None,
-                  return_lse: bool = False, split: int = 0, workspace=None, stream=None):
-    """attn_prefill_chunk: q [B,Hq,T,D] (rotated) against the cache prefix;
-    kv_len (int32 [B]) counts the chunk's own tokens -> o [B,Hq,T,D].  The
-    key ranges of ``split`` keys (0: default) use ``workspace`` (allocated if
-    not given and needed)."""
+                  return_lse: bool = False, split: int = 0, workspace=None, rope_theta: float = 0.0,
+                  stream=None):
+    """attn_prefill_chunk: q [B,Hq,T,D] against the cache prefix; kv_len
+    (int32 [B]) counts the chunk's own tokens -> o [B,Hq,T,D].  With
+    ``rope_theta`` > 0 the kernel rotates q to the chunk's positions (the
+    cached K rows already rotated); otherwise q is used as given.  The key
+    ranges of ``split`` keys (0: default) use ``workspace`` (allocated if not
+    given and needed)."""
     _ndim(q, "q", 4)
     _ndim(k_cache, "k_cache", 4)
     B, Hq, T, D = q.shape
@@ -231,7 +234,8 @@ def prefill_chunk(q, k_cache, v_cache, kv_len, softmax_scale: float, out_dtype=N
     _lib.check(_lib.lib().attn_prefill_chunk(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(kv_len, "kv_len"),
         _dev(out, "out"), _dev(lse, "lse") if lse is not None else None, ws_ptr, ws_bytes, B, Hq, Hkv, T, D,
-        cap, int(split), _dtype_code(q), _dtype_code(out), float(softmax_scale), _stream(stream)))
+        cap, int(split), _dtype_code(q), _dtype_code(out), float(softmax_scale), float(rope_theta),
+        _stream(stream)))
     return (out, lse) if return_lse else out
 
 

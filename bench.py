@@ -254,7 +254,6 @@ def decode_neighbours(iters=50):
     q, k, v = [t.to(dev) for t in prefill_inputs(B, Hq, Hkv, S, D, "bf16")]
     chunks = [(q[:, :, c:c + T].contiguous(), k[:, :, c:c + T].contiguous(), v[:, :, c:c + T].contiguous())
               for c in range(0, S, T)]
-    qb = [c[0].clone() for c in chunks]  # rotated in place each run: restored from chunks first
     kc = torch.empty((B, Hkv, S, D), dtype=torch.bfloat16, device=dev)
     vc = torch.empty_like(kc)
     Lc = torch.zeros(B, dtype=torch.int32, device=dev)
@@ -262,12 +261,13 @@ def decode_neighbours(iters=50):
     wsc = torch.empty(max(1, attn.prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, S)), dtype=torch.uint8,
                       device=dev)
 
+    # per chunk: append K (rotated) and V, advancing kv_len (one kernel), then
+    # the chunk's attention with its queries rotated in the kernel
     def chunked():
         Lc.zero_()
-        for (qc, kk, vv), qr, oo in zip(chunks, qb, oc):
-            qr.copy_(qc)
-            attn.kv_append(kk, vv, kc, vc, Lc, rope_theta=10000.0, q=qr)
-            attn.prefill_chunk(qr, kc, vc, Lc, scale, out=oo, workspace=wsc)
+        for (qc, kk, vv), oo in zip(chunks, oc):
+            attn.kv_append(kk, vv, kc, vc, Lc, rope_theta=10000.0)
+            attn.prefill_chunk(qc, kc, vc, Lc, scale, out=oo, workspace=wsc, rope_theta=10000.0)
     fo = torch.empty_like(q)
     fws = torch.empty(attn.prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, torch.bfloat16, 10000.0),
                       dtype=torch.uint8, device=dev)

@@ -325,7 +325,10 @@ attn_status attn_combine_splits(const float* o_part, const float* lse_part, void
  *
  * attn_prefill_chunk attends a chunk of T query rows per sequence to the
  * cache prefix:
- *   q       [B, Hq, T, D]      dtype (already rotated, e.g. by attn_kv_append)
+ *   q       [B, Hq, T, D]      dtype; with rope_theta > 0 the kernel rotates
+ *           row t to its position (below) as in attn_prefill_gqa_rope, in
+ *           registers (q itself is not written); with rope_theta <= 0 q is
+ *           used as given (e.g. already rotated by attn_kv_append)
  *   k_cache, v_cache [B, Hkv, cap, D]  dtype (K already rotated)
  *   kv_len  [B] int32 device memory: key count INCLUDING the chunk's own
  *           tokens (clamped to [0, cap])
@@ -340,7 +343,8 @@ attn_status attn_combine_splits(const float* o_part, const float* lse_part, void
  * 256-byte aligned; 0 bytes, workspace may be NULL, when one range covers
  * cap) and the combine kernel merges them.
  * dtype ATTN_BF16 or ATTN_F16 (others: ATTN_ERR_UNSUPPORTED); D 64 or 128;
- * T <= cap; scale a positive finite number; ATTN_ERR_WORKSPACE if the
+ * T <= cap; scale a positive finite number; rope_theta not NaN, and with
+ * RoPE cap <= 65536 (else ATTN_ERR_UNSUPPORTED); ATTN_ERR_WORKSPACE if the
  * workspace is missing or too small.  One or two kernels on `stream`.
  * ------------------------------------------------------------------------ */
 attn_status attn_kv_append(const void* k_new, const void* v_new, void* q, void* k_cache,
@@ -352,7 +356,7 @@ attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v
                                const int32_t* kv_len, void* o, float* lse, void* workspace,
                                size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D,
                                int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
-                               float softmax_scale, hipStream_t stream);
+                               float softmax_scale, float rope_theta, hipStream_t stream);
 
 #ifdef __cplusplus
 }

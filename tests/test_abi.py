@@ -242,14 +242,16 @@ def test_kv_append_rejects(lib):
 
 def test_prefill_chunk_rejects(lib):
     def chunk(q=P, kc=P, vc=P, L=P, o=P2, lse=None, ws=P, wsb=None, B=2, Hq=16, Hkv=4, T=32, D=128, cap=2056,
-              split=0, dt=_lib.ATTN_BF16, odt=_lib.ATTN_BF16, scale=0.088):
+              split=0, dt=_lib.ATTN_BF16, odt=_lib.ATTN_BF16, scale=0.088, theta=0.0):
         if wsb is None:
             wsb = lib.attn_prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split)
         return lib.attn_prefill_chunk(q, kc, vc, L, o, lse, ws, wsb, B, Hq, Hkv, T, D, cap, split, dt, odt, scale,
-                                      None)
+                                      theta, None)
     assert chunk(L=None) == 1 and chunk(o=None) == 1
     assert chunk(T=0) == 2 and chunk(T=3000) == 2 and chunk(Hq=6, Hkv=4) == 2 and chunk(split=100) == 2
     assert chunk(scale=0.0) == 2 and chunk(scale=float("nan")) == 2
+    assert chunk(theta=float("nan")) == 2 and chunk(theta=float("inf")) == 2
+    assert chunk(theta=10000.0, cap=70000, T=32) == 6  # RoPE positions past 2^16
     assert chunk(dt=_lib.ATTN_F32) == 6 and chunk(dt=_lib.ATTN_FP8_E5M2) == 6 and chunk(D=96) == 6
     assert chunk(odt=_lib.ATTN_FP8_E5M2) == 3 and chunk(dt=8) == 3
     assert chunk(q=ODD) == 4 and chunk(L=P + 2) == 4 and chunk(lse=P + 2) == 4

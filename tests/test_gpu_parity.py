@@ -748,10 +748,14 @@ def test_prefill_chunk_matches_oracle(attn, dtype, D, Hq, Hkv, T, split):
     assert np.max(np.abs(got_lse[~dead] - want_lse[~dead])) <= TOL[dtype]
 
 
-def test_chunked_prefill_pipeline_equals_fused_prefill(attn):
+@pytest.mark.parametrize("q_rot", ["append", "kernel"])
+def test_chunked_prefill_pipeline_equals_fused_prefill(attn, q_rot):
     """The C2 prompt (S=300 here) prefilled chunk by chunk (kv_append with
     RoPE, then prefill_chunk per 32-row chunk) against the oracle's one-shot
-    causal RoPE prefill and against the fused GPU prefill."""
+    causal RoPE prefill and against the fused GPU prefill.  The queries are
+    rotated either by kv_append (in place) or by the chunk kernel (q as
+    stored, rope_theta given to prefill_chunk; kv_append then moves only K
+    and V, in one workgroup that also advances kv_len)."""
     B, Hq, Hkv, S, D, T, cap = 1, 32, 8, 300, 128, 32, 320
     q, k, v = prefill_inputs(B, Hq, Hkv, S, D, "bf16", seed=81)
     scale = 1 / math.sqrt(D)
@@ -764,9 +768,15 @@ def test_chunked_prefill_pipeline_equals_fused_prefill(attn):
     for c0 in range(0, S, T):
         c1 = min(S, c0 + T)
         qc = dq[:, :, c0:c1].contiguous()
-        attn.kv_append(dk[:, :, c0:c1].contiguous(), dv[:, :, c0:c1].contiguous(), kc, vc, kv_len,
-                       rope_theta=10000.0, q=qc)
-        outs.append(attn.prefill_chunk(qc, kc, vc, kv_len, scale))
+        if q_rot == "append":
+            attn.kv_append(dk[:, :, c0:c1].contiguous(), dv[:, :, c0:c1].contiguous(), kc, vc, kv_len,
+                           rope_theta=10000.0, q=qc)
+            outs.append(attn.prefill_chunk(qc, kc, vc, kv_len, scale))
+        else:
+            attn.kv_append(dk[:, :, c0:c1].contiguous(), dv[:, :, c0:c1].contiguous(), kc, vc, kv_len,
+                           rope_theta=10000.0)
+            outs.append(attn.prefill_chunk(qc, kc, vc, kv_len, scale, rope_theta=10000.0))
+            assert torch.equal(qc, dq[:, :, c0:c1])  # q itself is not written
     got = torch.cat(outs, dim=2)
     assert kv_len.item() == S
     want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), scale, True, 10000.0)
