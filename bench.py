@@ -289,8 +289,9 @@ def sweep(scale):
     """Every tile configuration per shape; gap of the global configuration to the best one.
 
     Prefill: attn_prefill_gqa_rope_with_config ids (the global one is
-    GLOBAL_CONFIG for 16-bit inputs; fp8 inputs have two configurations, 0
-    with P in e4m3 (their default) and 1 with P in f16), timed in
+    GLOBAL_CONFIG, the software-pipelined kernel, for 16-bit and fp8 inputs;
+    fp8 inputs also have configuration 0, the 4-wave kernel with P in e4m3,
+    and 1, P in f16), timed in
     SWEEP_ROUNDS interleaved rounds (seeded random order), median per
     configuration.  Decode: the split size (global = the library default),
     hipGraph mode, cold caches."""
@@ -311,8 +312,10 @@ def sweep(scale):
               ("mha_D128_causal_N2048_f16", (4, 32, 32, 2048, 128, "f16", True, 0.0, torch.float16), all16, GLOBAL_CONFIG),
               ("mha_D64_noncausal_N8192_f16", (4, 32, 32, 8192, 64, "f16", False, 0.0, torch.float16), all16,
                GLOBAL_CONFIG),
-              ("mha_D64_noncausal_N4096_fp8", (4, 32, 32, 4096, 64, "fp8_e5m2", False, 0.0, torch.float16), [0, 1], 0),
-              ("mha_D128_causal_N4096_fp8", (4, 32, 32, 4096, 128, "fp8_e5m2", True, 0.0, torch.float16), [0, 1], 0)]
+              ("mha_D64_noncausal_N4096_fp8", (4, 32, 32, 4096, 64, "fp8_e5m2", False, 0.0, torch.float16), [0, 1, 7],
+               GLOBAL_CONFIG),
+              ("mha_D128_causal_N4096_fp8", (4, 32, 32, 4096, 128, "fp8_e5m2", True, 0.0, torch.float16), [0, 1, 7],
+               GLOBAL_CONFIG)]
     for name, (B, Hq, Hkv, S, D, dt, causal, theta, odt), confs, glob in shapes:
         q, k, v = [t.to(dev) for t in prefill_inputs(B, Hq, Hkv, S, D, dt, seed=S)]
         o = torch.empty(q.shape, dtype=odt, device=dev)

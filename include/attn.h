@@ -233,7 +233,7 @@ attn_status attn_decode_gqa(const void* q, const void* k_cache, const void* v_ca
  *   Limit: attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split) must not
  *   exceed 8 MiB (8388608 bytes), else ATTN_ERR_WORKSPACE and nothing is
  *   launched.  The default split at capacity 2056 (five partial parts of
- *   128 floats per query row) fits up to B * Hq = 3276 rows.
+ *   128 floats per query row) fits up to B * Hq = 3251 rows.
  *   Every call on one GPU shares that GPU's array: calls that overlap on one
  *   GPU (different streams or host threads) race and must be ordered by the
  *   caller.  The array needs no clearing between calls.

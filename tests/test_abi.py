@@ -281,3 +281,11 @@ def test_binding_rejects_cpu_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         _lib.load(str(tmp_path / "libattn.so"))
+
+
+def test_noalloc_documented_limit(lib):
+    """The allocation-free GQA decode's static array is 8 MiB: at the default
+    split and capacity 2056 its parts fit B * Hq = 3251 query rows and not
+    one more (the figure the header states)."""
+    need = lambda rows: lib.attn_decode_gqa_workspace_bytes(1, rows, 2056, 128, 0)  # noqa: E731
+    assert need(3251) <= 8 << 20 < need(3252)
