@@ -191,18 +191,23 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src + (size_t)min(key0, p.S) * ROWB), (short)0,
                                                range, kBufferRsrcWord3);
     };
-    // load u (0..IPW-1) of this wave's share of a tile
-    auto dma1 = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* dst, const int* loff, int u) {
-      // this wave's first row of the stage; opaque here, so the compiler
-      // forms the LDS address per load instead of keeping all of them
+    // this wave's first row of a stage, made opaque by the caller once per
+    // group of loads, so the compiler forms each load's LDS address with one
+    // scalar add instead of keeping all of them
+    auto wave_row = [&]() {
       int wrow = hoff + wq * (RPI * IPW * ROWB);
       asm volatile("" : "+s"(wrow));
+      return wrow;
+    };
+    // load u (0..IPW-1) of this wave's share of a tile
+    auto dma1 = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* dst, const int* loff, int u, int wrow) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_AS(void, dst + wrow + RPI * u * ROWB), 16, loff[u], 0, 0, 0);
     };
     auto dma = [&](const uint8_t* src, uint8_t* dst, const int* loff, int t) {
       const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src, t);
+      const int wrow = wave_row();
 #pragma unroll
-      for (int u = 0; u < IPW; ++u) dma1(rs, dst, loff, u);
+      for (int u = 0; u < IPW; ++u) dma1(rs, dst, loff, u, wrow);
     };
 
     // ---- Q fragments (B operand of S^T = K Q^T), rotated (RoPE) and
@@ -282,11 +287,11 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
       const u32x2 a1 = __builtin_bit_cast(u32x2, x1), a2 = __builtin_bit_cast(u32x2, x2);
       return u32x4{a1[0], a1[1], a2[0], a2[1]};
     };
-    // tiles crossing the diagonal or the sequence end need the mask
-    auto needs_mask = [&](int t) {
-      const int key0 = t * BN;
-      return (key0 + BN > p.S) || (CAUSAL && key0 + BN - 1 > pw0);
-    };
+    // tiles crossing the diagonal or the sequence end need the mask: tile t
+    // (keys t BN .. t BN + BN - 1) does iff t BN + BN > S or (causal) its last
+    // key lies past the wave's first row pw0, i.e. iff t >= t_mask
+    const int t_mask = CAUSAL ? min(p.S / BN, (pw0 + 1) / BN) : p.S / BN;
+    auto needs_mask = [&](int t) { return t >= t_mask; };
     // mask of key tile t: keys past the causal bound or the sequence -> -inf
     auto mask = [&](f32x16* s, int t) {
       const int lim = (CAUSAL ? min(qpos, p.S - 1) : p.S - 1) - t * BN - 4 * hh;
@@ -350,6 +355,7 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
     auto s_phase = [&](auto stc, f32x16* s, const f32x16& base, f32x16* sp, bool loads,
                        __amdgpu_buffer_rsrc_t krs, uint8_t* kdst, __amdgpu_buffer_rsrc_t vrs, uint8_t* vdst) {
       const uint8_t* kb = kst(stc) + hoff;
+      const int wrow = loads ? wave_row() : 0;
       constexpr int KPF = ATTN_SP_KPF;  // K fragments read this many MFMAs ahead
       u32x4 fa[KPF + 1];
 #pragma unroll
@@ -369,8 +375,8 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
         if (loads) {
 #pragma unroll
           for (int u = 0; u < IPW; ++u) {
-            if (j == 1 + 2 * u) dma1(krs, kdst, dk, u);
-            if (j == NJS / 2 + 1 + 2 * u) dma1(vrs, vdst, dv, u);
+            if (j == 1 + 2 * u) dma1(krs, kdst, dk, u, wrow);
+            if (j == NJS / 2 + 1 + 2 * u) dma1(vrs, vdst, dv, u, wrow);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
