@@ -70,6 +70,13 @@ using ic = std::integral_constant<int, N>;
 #ifndef ATTN_SP_VPF
 #define ATTN_SP_VPF 2
 #endif
+// row sum of a packed pair of probabilities: 2 = the two fp32 values added
+// before rounding (two adds that issue beside the MFMAs); 0 = one dot product
+// of the rounded pair against ones (a dot product next to an MFMA stalls the
+// wave for about half an MFMA); 1 = the two rounded halves widened and added
+#ifndef ATTN_SP_LSUM
+#define ATTN_SP_LSUM 2
+#endif
 
 // HALVES = 2: 8-wave workgroups whose two halves (4 waves each, one wave of
 // each on every SIMD) take alternate key tiles of the same query rows, each
@@ -153,6 +160,25 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
   const int half_items = (n_items + 1) / 2;
   const int item0 = (CAUSAL && !PAIR && wg >= half_items) ? n_items - 1 - (wg - half_items) : wg;
 
+  // RoPE frequencies of this lane's Q elements (element 16 kk + 8 hh + j of
+  // the row pairs with element + D/2; kk < NKK/2, j < 8), read once for every
+  // item: the reads are issued before any load of the first item, so waiting
+  // for them never waits for that item's K/V DMA as well (the vector memory
+  // counter retires in order).  The 8-wave kernel, which has half the
+  // registers, reads them per item.
+  constexpr bool RQ_HOIST = RQ && HALVES == 1;
+  constexpr int NRF = RQ_HOIST ? NKK * 4 : 1;
+  float rfh[NRF], rfl[NRF];
+  if constexpr (RQ_HOIST) {
+#pragma unroll
+    for (int kk = 0; kk < NKK / 2; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        rfh[8 * kk + j] = p.rope_fhi[16 * kk + 8 * hh + j];
+        rfl[8 * kk + j] = p.rope_flo[16 * kk + 8 * hh + j];
+      }
+  }
+
 #pragma unroll 1
   for (int itn = 0; itn < n_my; ++itn) {
     // every wave is done with the previous item's LDS stages before any
@@ -214,10 +240,13 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
     //      multiplied by softmax_scale * log2(e), one rounding to the input type ----
     uint32_t qf[NKK * 4];
     {
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head) * p.S + qpos) * D;
+      // rows past the sequence end (a ragged last tile) read row S - 1
+      // instead: their results are never stored, and the loads need no branch
+      const int qld = min(qpos, p.S - 1);
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head) * p.S + qld) * D;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 w = qpos < p.S ? ldg16(qrow + 16 * kk + 8 * hh) : u32x4{0, 0, 0, 0};
+        const u32x4 w = ldg16(qrow + 16 * kk + 8 * hh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
       }
@@ -249,7 +278,9 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
               const int fi = 16 * kk + 8 * hh + 2 * e + s;
-              const float rev = __builtin_amdgcn_fractf((float)qpos * p.rope_fhi[fi]) + (float)qpos * p.rope_flo[fi];
+              const float fh = RQ_HOIST ? rfh[(8 * kk + 2 * e + s) % NRF] : p.rope_fhi[fi];
+              const float fl = RQ_HOIST ? rfl[(8 * kk + 2 * e + s) % NRF] : p.rope_flo[fi];
+              const float rev = __builtin_amdgcn_fractf((float)qpos * fh) + (float)qpos * fl;
               const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
               const float x1 = Tag::to_f32(s ? (w1 >> 16) : (w1 & 0xffff));
               const float x2 = Tag::to_f32(s ? (w2 >> 16) : (w2 & 0xffff));
@@ -274,7 +305,7 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
     f32x16 sA[NB], sB[NB];  // score tiles of even / odd key tiles (exponent domain, minus the reference)
     f32x16 negm = {};       // -reference of this lane's row, the first S MFMA's accumulator input
     float m_ref = 0.f;      // reference (exponent domain), equal in both lanes of a row
-    float l_run = 0.f;      // sum over this lane's keys of the rounded probabilities
+    float l_run = 0.f;      // sum over this lane's keys of the probabilities
     uint32_t pf[CPB][4];    // probabilities of the tile being multiplied into V (B operand)
 
     auto krd = [&](const uint8_t* kb, int j) {
@@ -312,7 +343,9 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
       const int nb = v / 16, r = v % 16;
       const uint32_t pk = Tag::pack2(e0, e1);
       pf[2 * nb + (r >> 3)][(r & 7) >> 1] = pk;
-      l_run = Tag::sum2(pk, l_run);
+      if constexpr (ATTN_SP_LSUM == 0) l_run = Tag::sum2(pk, l_run);
+      else if constexpr (ATTN_SP_LSUM == 1) l_run = (l_run + Tag::to_f32(pk & 0xffff)) + Tag::to_f32(pk >> 16);
+      else l_run = (l_run + e0) + e1;
     };
     auto expv = [&](f32x16* s, int v) {
       float e0, e1;
@@ -548,18 +581,24 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
     const float inv = l > 0.f ? p.out_scale / l : 0.f;
     if (half == 0 && qpos < p.S && n_w > 0) {
       const size_t row = ((size_t)b * p.Hq + head) * p.S + qpos;
+      // one branch on the output type for the whole row, not one per store
+      auto store_row = [&](auto odt) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          float o4[4];
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float o4[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            o4[e] = HALVES == 2 ? (acc_o[db][r] * f0 + xch[(db * 16 + r) * 64 + lane] * f1) * inv : acc_o[db][r] * inv;
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g4 + e;
+              o4[e] = HALVES == 2 ? (acc_o[db][r] * f0 + xch[(db * 16 + r) * 64 + lane] * f1) * inv : acc_o[db][r] * inv;
+            }
+            store4(p.o, row * D + 32 * db + 8 * g4 + 4 * hh, decltype(odt)::value, o4[0], o4[1], o4[2], o4[3]);
           }
-          store4(p.o, row * D + 32 * db + 8 * g4 + 4 * hh, p.out_dtype, o4[0], o4[1], o4[2], o4[3]);
-        }
+      };
+      if (p.out_dtype == ATTN_BF16) store_row(ic<ATTN_BF16>{});
+      else if (p.out_dtype == ATTN_F16) store_row(ic<ATTN_F16>{});
+      else store_row(ic<ATTN_F32>{});
       if (p.lse && hh == 0) p.lse[row] = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : kNegInf;
     }
   }
