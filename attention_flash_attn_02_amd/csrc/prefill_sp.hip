@@ -579,7 +579,57 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
       }
     }
     const float inv = l > 0.f ? p.out_scale / l : 0.f;
-    if (half == 0 && qpos < p.S && n_w > 0) {
+    if constexpr (HALVES == 1) {
+      // O / l leaves through LDS, so that every global store writes 16-byte
+      // pieces of whole rows (a lane's accumulator holds 4-element pieces of
+      // one row: stored directly, each store instruction would touch 32 rows).
+      // Wave wq transposes through stage array wq once every wave is past its
+      // key loop and its loads into the stages have landed; the barrier at the
+      // start of the next item keeps that item's loads out until all waves
+      // have read their rows back.
+      uint8_t* area = wq == 0 ? k0 : wq == 1 ? k1 : wq == 2 ? v0 : v1;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("s_barrier" ::: "memory");
+      if (n_w > 0) {
+        // lane indices made opaque here: the addresses derived from them are
+        // then formed in the epilogue, not hoisted out of the item loop (where
+        // they would hold registers through the whole key loop)
+        int lm = m, ln = lane;
+        asm volatile("" : "+v"(lm), "+v"(ln));
+        auto stage_out = [&](auto odt) {
+          constexpr int OD = decltype(odt)::value;
+          constexpr int ES = OD == ATTN_F32 ? 4 : 2;  // bytes per output element
+          constexpr int RB = D * ES;                  // bytes per output row
+          constexpr int CPR = RB / 16;                // 16-byte pieces per row (XOR-swizzled by row)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int byte = (32 * db + 8 * g4 + 4 * hh) * ES;
+              uint8_t* dst = area + lm * RB + 16 * ((byte / 16) ^ (lm % CPR)) + byte % 16;
+              const float o0 = acc_o[db][4 * g4] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
+              const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;
+              if constexpr (OD == ATTN_F32) *reinterpret_cast<f32x4*>(dst) = f32x4{o0, o1, o2, o3};
+              else if constexpr (OD == ATTN_BF16) *reinterpret_cast<u32x2*>(dst) = u32x2{Bf16Tag::pack2(o0, o1), Bf16Tag::pack2(o2, o3)};
+              else *reinterpret_cast<u32x2*>(dst) = u32x2{F16Tag::pack2(o0, o1), F16Tag::pack2(o2, o3)};
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes are done before its reads
+          constexpr int RPR = 64 / CPR;  // rows per read instruction
+          uint8_t* obase = reinterpret_cast<uint8_t*>(p.o) + (((size_t)b * p.Hq + head) * p.S + pw0) * RB;
+#pragma unroll
+          for (int i = 0; i < 32 / RPR; ++i) {
+            const int r = RPR * i + ln / CPR, c = ln % CPR;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(area + r * RB + 16 * (c ^ (r % CPR)));
+            if (pw0 + r < p.S) *reinterpret_cast<u32x4*>(obase + (size_t)r * RB + 16 * c) = v;
+          }
+        };
+        if (p.out_dtype == ATTN_BF16) stage_out(ic<ATTN_BF16>{});
+        else if (p.out_dtype == ATTN_F16) stage_out(ic<ATTN_F16>{});
+        else stage_out(ic<ATTN_F32>{});
+        if (p.lse && hh == 0 && qpos < p.S)
+          p.lse[((size_t)b * p.Hq + head) * p.S + qpos] = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : kNegInf;
+      }
+    } else if (half == 0 && qpos < p.S && n_w > 0) {
       const size_t row = ((size_t)b * p.Hq + head) * p.S + qpos;
       // one branch on the output type for the whole row, not one per store
       auto store_row = [&](auto odt) {
@@ -591,7 +641,7 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g4 + e;
-              o4[e] = HALVES == 2 ? (acc_o[db][r] * f0 + xch[(db * 16 + r) * 64 + lane] * f1) * inv : acc_o[db][r] * inv;
+              o4[e] = (acc_o[db][r] * f0 + xch[(db * 16 + r) * 64 + lane] * f1) * inv;
             }
             store4(p.o, row * D + 32 * db + 8 * g4 + 4 * hh, decltype(odt)::value, o4[0], o4[1], o4[2], o4[3]);
           }
