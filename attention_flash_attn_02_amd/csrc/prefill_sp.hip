@@ -615,13 +615,20 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
             }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes are done before its reads
           constexpr int RPR = 64 / CPR;  // rows per read instruction
+          // all reads first, then all stores; the buffer range ends at the
+          // sequence end, so rows past it are dropped without a branch
           uint8_t* obase = reinterpret_cast<uint8_t*>(p.o) + (((size_t)b * p.Hq + head) * p.S + pw0) * RB;
+          const __amdgpu_buffer_rsrc_t ors =
+              __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, min(p.S - pw0, 32) * RB, kBufferRsrcWord3);
+          u32x4 ov[32 / RPR];
 #pragma unroll
           for (int i = 0; i < 32 / RPR; ++i) {
             const int r = RPR * i + ln / CPR, c = ln % CPR;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(area + r * RB + 16 * (c ^ (r % CPR)));
-            if (pw0 + r < p.S) *reinterpret_cast<u32x4*>(obase + (size_t)r * RB + 16 * c) = v;
+            ov[i] = *reinterpret_cast<const u32x4*>(area + r * RB + 16 * (c ^ (r % CPR)));
           }
+#pragma unroll
+          for (int i = 0; i < 32 / RPR; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(ov[i], ors, (RPR * i + ln / CPR) * RB + 16 * (ln % CPR), 0, 0);
         };
         if (p.out_dtype == ATTN_BF16) stage_out(ic<ATTN_BF16>{});
         else if (p.out_dtype == ATTN_F16) stage_out(ic<ATTN_F16>{});

@@ -306,8 +306,11 @@ def test_prefill_short_sequences(attn, S):
     assert torch.equal(o[0, :, 0].cpu(), v[0, :, 0].repeat_interleave(4, dim=0))
 
 
-def test_prefill_out_dtype_f32_and_G8(attn):
-    q, k, v = prefill_inputs(1, 16, 2, 150, 128, "bf16", seed=5)
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_out_dtype_f32_and_G8(attn, D):
+    """fp32 output (stored through the kernel's LDS transpose with 4-byte
+    elements), eight query heads per KV head, a ragged sequence."""
+    q, k, v = prefill_inputs(1, 16, 2, 150, D, "bf16", seed=5)
     o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.09, causal=True, rope_theta=500.0, out_dtype=torch.float32)
     want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 0.09, True, 500.0)
     assert o.dtype == torch.float32
