@@ -2,7 +2,7 @@
 
 Python entry points (same names as the C calls, without the ``attn_`` prefix):
 prefill_gqa_rope, rope_rotate, decode_gqa, decode_gqa_noalloc, decode_mla,
-combine_splits, kv_append, prefill_chunk, and the workspace size queries;
+combine_splits, kv_append, prefill_chunk, prefill_chunk_step, and the workspace size queries;
 prefill_gqa_rope_unfused composes rope_rotate with the attention call.
 libattn.so is loaded on first use; every call raises ImportError if it has
 not been built (there is no other code path).
@@ -17,6 +17,7 @@ from .ops import (  # noqa: F401
     decode_mla_workspace_bytes,
     kv_append,
     prefill_chunk,
+    prefill_chunk_step,
     prefill_chunk_workspace_bytes,
     prefill_gqa_rope,
     prefill_gqa_rope_unfused,

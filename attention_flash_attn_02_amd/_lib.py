@@ -51,6 +51,9 @@ SIGNATURES = {
     "attn_prefill_chunk_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_float, _vp]),
+    "attn_prefill_chunk_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _c_int, _c_int,
+                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                         _c_float, _vp]),
 }
 
 

@@ -15,13 +15,21 @@
 
 namespace attn {
 
+// the cache-length advance a combine can carry (before any early exit: the
+// combine never reads kv_len, and every kernel that did has finished)
+__device__ inline void kv_advance(const KvAdvance& a) {
+  if (a.kv_len && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.B; i += blockDim.x) a.kv_len[i] = min(max(a.kv_len[i], 0) + a.T, a.cap);
+}
+
 // One thread per (row, 4 consecutive dims): every thread recomputes the
 // row's split weights from the (cached) lse values and then reads its float4
 // of every split with independent loads.  Requires D % 4 == 0.
 __global__ __launch_bounds__(256) void combine_kernel_v4(const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part,
                                                          void* __restrict__ o, float* __restrict__ lse_out,
-                                                         int R, int nsplit, int D, int out_dtype) {
+                                                         int R, int nsplit, int D, int out_dtype, KvAdvance adv) {
+  kv_advance(adv);
   const int d4n = D >> 2;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   if (t >= (long long)R * d4n) return;
@@ -70,7 +78,8 @@ template <int NS>
 __global__ __launch_bounds__(256) void combine_kernel_v4s(const float* __restrict__ o_part,
                                                           const float* __restrict__ lse_part,
                                                           void* __restrict__ o, float* __restrict__ lse_out,
-                                                          int R, int nsplit, int D, int out_dtype) {
+                                                          int R, int nsplit, int D, int out_dtype, KvAdvance adv) {
+  kv_advance(adv);
   const int d4n = D >> 2;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   if (t >= (long long)R * d4n) return;
@@ -172,7 +181,8 @@ void launch_combine_bf16_parts(const uint16_t* o_part, const float* lse_part, vo
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       void* __restrict__ o, float* __restrict__ lse_out,
-                                                      int R, int nsplit, int D, int out_dtype) {
+                                                      int R, int nsplit, int D, int out_dtype, KvAdvance adv) {
+  kv_advance(adv);
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= R) return;
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
-                    int out_dtype, hipStream_t stream, float* lse_out) {
+                    int out_dtype, hipStream_t stream, float* lse_out, KvAdvance adv) {
   if (D % 4 == 0) {
     const long long threads = (long long)R * (D / 4);
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
@@ -229,13 +239,13 @@ void launch_combine(const float* o_part, const float* lse_part, void* o, int R, 
     // parts was slower, 8.9 vs 7.6 us)
     if (nsplit <= 8 && ((long long)R * nsplit + 8) * D * 4 < (1LL << 31))
       hipLaunchKernelGGL(combine_kernel_v4s<8>, grid, block, 0, stream, o_part, lse_part, o, lse_out, R, nsplit, D,
-                         out_dtype);
+                         out_dtype, adv);
     else
       hipLaunchKernelGGL(combine_kernel_v4, grid, block, 0, stream, o_part, lse_part, o, lse_out, R, nsplit, D,
-                         out_dtype);
+                         out_dtype, adv);
   } else {
     hipLaunchKernelGGL(combine_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, o_part, lse_part, o, lse_out,
-                       R, nsplit, D, out_dtype);
+                       R, nsplit, D, out_dtype, adv);
   }
 }
 

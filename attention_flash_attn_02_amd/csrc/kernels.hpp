@@ -6,15 +6,27 @@
 
 namespace attn {
 
+// Advance of a static append cache's lengths, kv_len[b] = min(kv_len[b] + T,
+// cap) for b < B, done by a kernel that runs after every reader of kv_len in
+// the same step (kv_len null: none)
+struct KvAdvance {
+  int* kv_len = nullptr;
+  int B = 0, T = 0, cap = 0;
+};
+
 // Merge split partials o_part [R, nsplit, D] / lse_part [R, nsplit] into
 // o [R, D] (out_dtype) on `stream`; lse_out [R] (natural log), if given,
 // receives the merged log-sum-exp.
+// The combine also applies `adv` (first workgroup), when given.
 void launch_combine(const float* o_part, const float* lse_part, void* o, int R, int nsplit, int D,
-                    int out_dtype, hipStream_t stream, float* lse_out = nullptr);
+                    int out_dtype, hipStream_t stream, float* lse_out = nullptr, KvAdvance adv = {});
 
 // The same with the partial outputs stored as bf16 bits (o_part [R, nsplit, D]).
 void launch_combine_bf16_parts(const uint16_t* o_part, const float* lse_part, void* o, int R, int nsplit,
                                int D, int out_dtype, hipStream_t stream);
+
+// kv_len[b] = min(kv_len[b] + T, cap) as a launch of its own
+void launch_kv_advance(const KvAdvance& adv, hipStream_t stream);
 
 // Workspace layout of the decode calls: partial outputs first, then the
 // partial log-sum-exps, each 256-byte aligned.

@@ -29,11 +29,16 @@
 //     sequence first) so short tiles fill the tail of the launch.
 // fp32 inputs use a plain SIMT kernel (one query row per thread).
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "prefill_common.hpp"
 
 namespace attn {
+
+template <int N>
+using ic_t = std::integral_constant<int, N>;
 
 
 
@@ -621,8 +626,25 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
     const int head = kvh * p.G + hg * p.GP + (wq % p.GP);
     const int p0 = ptile * p.P;
     const int pw0 = p0 + (wq / p.GP) * 32;
+    // Q rows (B operand of S^T = K Q^T), loaded unrotated; in chunk mode
+    // before the key length is read, so that the two loads overlap
+    uint32_t qf[D / 4];
+    auto load_q = [&]() {
+      const int qp = pw0 + m;
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head) * p.S + min(qp, p.S - 1)) * D;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 w = ldg16(qrow + 16 * kk + 8 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
+      }
+    };
+    if (CHUNK) {
+      load_q();
+      __builtin_amdgcn_sched_barrier(0);  // (the scheduler would otherwise wait for the key length first)
+    }
     // key length and query position offset (plain prefill: S and 0)
-    const int Skv = CHUNK ? min(max(p.kv_len[b], 0), p.cap) : p.S;
+    const int Skv = CHUNK ? min(max(p.kv_len[b], 0) + p.kv_add, p.cap) : p.S;
     const int qoff = CHUNK ? Skv - p.S : 0;
     const int kend_all = CAUSAL ? max(0, min(Skv, qoff + p0 + p.P)) : Skv;
     // key range [kbeg, kend) of this item: all keys, or (chunk mode) split
@@ -756,14 +778,15 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
 
     // ---- Q fragments (B operand of S^T = K Q^T), loaded (and rotated) while
     //      the first tile's K/V loads are in flight ----
-    uint32_t qf[D / 4];
     {
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head) * p.S + qpos) * D;
+      if (!CHUNK) {
+        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head) * p.S + qpos) * D;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 w = qpos < p.S ? ldg16(qrow + 16 * kk + 8 * hh) : u32x4{0, 0, 0, 0};
+        for (int kk = 0; kk < NKK; ++kk) {
+          u32x4 w = qpos < p.S ? ldg16(qrow + 16 * kk + 8 * hh) : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
+          for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
+        }
       }
       if (RQ) {
 #pragma unroll
@@ -1058,7 +1081,63 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       // [rows, nsplit, D] / [rows, nsplit] for the combine step
       const bool to_ws = CHUNK && p.nsplit > 1;
       const size_t row = ((size_t)b * p.Hq + head) * p.S + qpos;
-      if (qpos < p.S) {
+      if constexpr (CHUNK) {
+        // chunk mode: O (or this key range's part of it) leaves through LDS,
+        // so that each store instruction writes 16-byte pieces of whole rows
+        // instead of touching 32 rows (a lane's accumulator holds 4-element
+        // pieces of one row).  Wave wq transposes through quarter wq of the
+        // stage memory once every wave is past its key loop; the item loop's
+        // barrier keeps the next item's loads out until all have read back.
+        uint8_t* area = smem + wq * TILEB;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        int lm = m, ln = lane;
+        asm volatile("" : "+v"(lm), "+v"(ln));  // keep the addresses below out of the item loop
+        auto stage_out = [&](auto odt) {
+          constexpr int OD = decltype(odt)::value;
+          constexpr int ES = OD == ATTN_F32 ? 4 : 2;
+          constexpr int RB = D * ES;    // bytes per output row
+          constexpr int CPR = RB / 16;  // 16-byte pieces per row (XOR-swizzled by row)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int byte = (32 * db + 8 * g4 + 4 * hh) * ES;
+              uint8_t* dst = area + lm * RB + 16 * ((byte / 16) ^ (lm % CPR)) + byte % 16;
+              const float o0 = acc_o[db][4 * g4] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
+              const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;
+              if constexpr (OD == ATTN_F32) *reinterpret_cast<f32x4*>(dst) = f32x4{o0, o1, o2, o3};
+              else if constexpr (OD == ATTN_BF16) *reinterpret_cast<u32x2*>(dst) = u32x2{Bf16Tag::pack2(o0, o1), Bf16Tag::pack2(o2, o3)};
+              else *reinterpret_cast<u32x2*>(dst) = u32x2{F16Tag::pack2(o0, o1), F16Tag::pack2(o2, o3)};
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes are done before its reads
+          constexpr int RPR = 64 / CPR;  // rows per read instruction
+          // destination row r of this wave: query row pw0 + r; parts of
+          // consecutive rows are nsplit pieces apart in the split workspace
+          const size_t rstride = (size_t)(to_ws ? p.nsplit : 1) * RB;
+          uint8_t* obase = reinterpret_cast<uint8_t*>(to_ws ? static_cast<void*>(p.ws_o) : p.o) +
+                           ((((size_t)b * p.Hq + head) * p.S + pw0) * (to_ws ? p.nsplit : 1) + (to_ws ? split : 0)) * RB;
+          u32x4 ov[32 / RPR];
+#pragma unroll
+          for (int i = 0; i < 32 / RPR; ++i) {
+            const int r = RPR * i + ln / CPR, c = ln % CPR;
+            ov[i] = *reinterpret_cast<const u32x4*>(area + r * RB + 16 * (c ^ (r % CPR)));
+          }
+#pragma unroll
+          for (int i = 0; i < 32 / RPR; ++i) {
+            const int r = RPR * i + ln / CPR, c = ln % CPR;
+            if (pw0 + r < p.S) *reinterpret_cast<u32x4*>(obase + (size_t)r * rstride + 16 * c) = ov[i];
+          }
+        };
+        if (to_ws || p.out_dtype == ATTN_F32) stage_out(ic_t<ATTN_F32>{});
+        else if (p.out_dtype == ATTN_BF16) stage_out(ic_t<ATTN_BF16>{});
+        else stage_out(ic_t<ATTN_F16>{});
+        if (qpos < p.S && hh == 0) {
+          const float lse_row = l > 0.f ? (Mu + __log2f(l)) * kLn2 : kNegInf;
+          if (to_ws) p.ws_lse[row * p.nsplit + split] = lse_row;
+          else if (p.lse) p.lse[row] = lse_row;
+        }
+      } else if (qpos < p.S) {
         const size_t obase = to_ws ? (row * p.nsplit + split) * D : row * D;
         void* const obuf = to_ws ? static_cast<void*>(p.ws_o) : p.o;
         const int odt = to_ws ? (int)ATTN_F32 : p.out_dtype;
@@ -1987,11 +2066,14 @@ static void launch_chunk_kernel(const PrefillParams& p, bool rope, dim3 grid, di
   else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, 0, 1, true>), grid, block, 0, st, p);
 }
 
-extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
-                                          const int32_t* kv_len, void* o, float* lse, void* workspace,
-                                          size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D,
-                                          int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
-                                          float softmax_scale, float rope_theta, hipStream_t stream) {
+// the chunk attention: kv_len[b] + kv_add keys per sequence; `adv`, when
+// given, advances kv_len once every reader is done (in the combine, or as a
+// launch of its own when there is a single key range)
+static attn_status chunk_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                                   void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq,
+                                   int Hkv, int T, int D, int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
+                                   float softmax_scale, float rope_theta, int kv_add, KvAdvance adv,
+                                   hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !kv_len || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || cap <= 0 || T > cap) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -2028,6 +2110,7 @@ extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, co
   p.out_dtype = out_dtype;
   p.halves = 1;
   p.kv_len = kv_len;
+  p.kv_add = kv_add;
   p.cap = cap;
   p.nsplit = nsplit;
   p.split_keys = sk;
@@ -2054,6 +2137,66 @@ extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, co
     if (D == 64) launch_chunk_kernel<F16Tag, 64>(p, rope, grid, block, stream);
     else launch_chunk_kernel<F16Tag, 128>(p, rope, grid, block, stream);
   }
-  if (nsplit > 1) launch_combine(p.ws_o, p.ws_lse, o, (int)R, nsplit, D, out_dtype, stream, lse);
+  if (nsplit > 1) launch_combine(p.ws_o, p.ws_lse, o, (int)R, nsplit, D, out_dtype, stream, lse, adv);
+  else if (adv.kv_len) launch_kv_advance(adv, stream);
   return attn_host::launch_status();
+}
+
+extern "C" attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* kv_len, void* o, float* lse, void* workspace,
+                                          size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D,
+                                          int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
+                                          float softmax_scale, float rope_theta, hipStream_t stream) {
+  return chunk_attention(q, k_cache, v_cache, kv_len, o, lse, workspace, workspace_bytes, B, Hq, Hkv, T, D, cap,
+                         split, dtype, out_dtype, softmax_scale, rope_theta, 0, KvAdvance{}, stream);
+}
+
+extern "C" attn_status attn_prefill_chunk_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                               void* v_cache, int32_t* kv_len, void* o, float* lse,
+                                               void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                                               int T, int D, int cap, int split, attn_dtype dtype,
+                                               attn_dtype out_dtype, float softmax_scale, float rope_theta,
+                                               hipStream_t stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !kv_len || !o) return ATTN_ERR_NULL;
+  // the attention's checks first (they cover every shape the append takes),
+  // so that a rejected call changes nothing
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || cap <= 0 || T > cap || Hq % Hkv != 0)
+    return ATTN_ERR_SHAPE;
+  if (split > 0 && (split % 64 != 0)) return ATTN_ERR_SHAPE;
+  if (dtype < ATTN_F32 || dtype > ATTN_FP8_E5M2) return ATTN_ERR_DTYPE;
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_F16 && out_dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 3.0e38f)) return ATTN_ERR_SHAPE;
+  if (rope_theta != rope_theta || !(rope_theta < 3.0e38f)) return ATTN_ERR_SHAPE;
+  if (rope_theta > 0.f && cap > 65536) return ATTN_ERR_UNSUPPORTED;
+  if (!attn_host::aligned(q, 16) || !attn_host::aligned(k_new, 16) || !attn_host::aligned(v_new, 16) ||
+      !attn_host::aligned(k_cache, 16) || !attn_host::aligned(v_cache, 16) || !attn_host::aligned(o, 16) ||
+      !attn_host::aligned(kv_len, 4) || (lse && !attn_host::aligned(lse, 4)))
+    return ATTN_ERR_ALIGN;
+  if ((long long)B * Hkv * cap * D > (1LL << 40) || (long long)B * Hq * T * D > (1LL << 40) ||
+      (long long)Hq * T * D > (1LL << 30))
+    return ATTN_ERR_SHAPE;
+  {
+    const int sk = chunk_split_keys(B, Hq, Hkv, T, cap, split);
+    const int nsplit = (cap + sk - 1) / sk;
+    const long long R = (long long)B * Hq * T;
+    if (nsplit > 1) {
+      const SplitWorkspace w = split_workspace(R, nsplit, D);
+      if (!workspace || workspace_bytes < w.total) return ATTN_ERR_WORKSPACE;
+      if (!attn_host::aligned(workspace, 256)) return ATTN_ERR_ALIGN;
+      if (R > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    }
+    const int G = Hq / Hkv, GP = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1, P = 128 / GP;
+    if ((long long)((T + P - 1) / P) * B * Hkv * (G / GP) * nsplit > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  }
+  // 1: the chunk's K (rotated to its slots) and V into the caches, kv_len unchanged
+  attn_status st = attn_kv_append(k_new, v_new, nullptr, k_cache, v_cache, kv_len, B, Hkv, 0, T, D, cap, dtype,
+                                  rope_theta, 0, stream);
+  if (st != ATTN_OK) return st;
+  // 2: the attention over kv_len + T keys; 3: the combine, which also
+  // advances kv_len by T
+  return chunk_attention(q, k_cache, v_cache, kv_len, o, lse, workspace, workspace_bytes, B, Hq, Hkv, T, D, cap,
+                         split, dtype, out_dtype, softmax_scale, rope_theta, T, KvAdvance{kv_len, B, T, cap},
+                         stream);
 }

@@ -35,7 +35,8 @@ struct PrefillParams {
   int pingpong;  // 8-wave kernel: the two halves run half a key tile apart (see PP)
   int regstage;  // 4-wave kernel: K and V tiles staged through registers (see RS)
   // chunked prefill against a cache prefix (prefill_fwd_kernel<..., CHUNK>)
-  const int* kv_len;  // [B] key lengths including the chunk, device memory
+  const int* kv_len;  // [B] key lengths (with kv_add: the chunk's tokens), device memory
+  int kv_add;         // added to kv_len[b]: 0, or the chunk length when kv_len excludes the chunk
   int cap;            // cache slots per head
   int nsplit;         // key ranges per item (1: results go straight to o / lse)
   int split_keys;     // keys per range, a multiple of 64

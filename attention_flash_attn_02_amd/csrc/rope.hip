@@ -17,6 +17,7 @@
 // is read and written by the same thread).
 
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace attn {
 
@@ -180,6 +181,11 @@ __global__ __launch_bounds__(256) void advance_kernel(int* kv_len, int B, int T,
   if (b < B) kv_len[b] = min(max(kv_len[b], 0) + T, cap);
 }
 
+void launch_kv_advance(const KvAdvance& adv, hipStream_t stream) {
+  hipLaunchKernelGGL(advance_kernel, dim3((unsigned)((adv.B + 255) / 256)), dim3(256), 0, stream, adv.kv_len, adv.B,
+                     adv.T, adv.cap);
+}
+
 }  // namespace attn
 
 using namespace attn;
@@ -247,7 +253,6 @@ extern "C" attn_status attn_kv_append(const void* k_new, const void* v_new, void
   if (dtype == ATTN_BF16) hipLaunchKernelGGL((append_kernel<Bf16Tag>), grid, block, 0, stream, p);
   else if (dtype == ATTN_F16) hipLaunchKernelGGL((append_kernel<F16Tag>), grid, block, 0, stream, p);
   else hipLaunchKernelGGL((append_kernel<F32Elem>), grid, block, 0, stream, p);
-  if (advance && grid.y > 1)
-    hipLaunchKernelGGL(advance_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, kv_len, B, T, cap);
+  if (advance && grid.y > 1) launch_kv_advance(KvAdvance{kv_len, B, T, cap}, stream);
   return attn_host::launch_status();
 }

@@ -239,6 +239,45 @@ def prefill_chunk(q, k_cache, v_cache, kv_len, softmax_scale: float, out_dtype=N
     return (out, lse) if return_lse else out
 
 
+def prefill_chunk_step(q, k_new, v_new, k_cache, v_cache, kv_len, softmax_scale: float, out_dtype=None,
+                       out=None, return_lse: bool = False, split: int = 0, workspace=None,
+                       rope_theta: float = 0.0, stream=None):
+    """attn_prefill_chunk_step: one chunked-prefill step into a static append
+    cache.  q [B,Hq,T,D] (not rotated), k_new/v_new [B,Hkv,T,D] are appended
+    at slots kv_len[b].. (K rotated there when rope_theta > 0), q attends to
+    the cache prefix including the chunk, and kv_len (int32 [B], EXCLUDING
+    the chunk on entry) advances by T -> o [B,Hq,T,D]."""
+    _ndim(q, "q", 4)
+    _ndim(k_new, "k_new", 4)
+    _ndim(k_cache, "k_cache", 4)
+    B, Hq, T, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    _shape(k_new, "k_new", (B, Hkv, T, D), q.dtype)
+    _shape(v_new, "v_new", (B, Hkv, T, D), q.dtype)
+    _shape(k_cache, "k_cache", (B, Hkv, cap, D), q.dtype)
+    _shape(v_cache, "v_cache", (B, Hkv, cap, D), q.dtype)
+    _shape(kv_len, "kv_len", (B,), torch.int32)
+    if out is not None:
+        _shape(out, "out", (B, Hq, T, D), out_dtype or out.dtype)
+    need = prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split)
+    _check_workspace(workspace, need)
+    _same_device(q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, kv_len=kv_len, out=out,
+                 workspace=workspace)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    if need > 0:
+        workspace = _workspace(workspace, need, q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check(_lib.lib().attn_prefill_chunk_step(
+        _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(kv_len, "kv_len"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else None, ws_ptr, ws_bytes, B, Hq, Hkv, T, D, cap, int(split),
+        _dtype_code(q), _dtype_code(out), float(softmax_scale), float(rope_theta), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
 def decode_gqa_workspace_bytes(B, Hq, cap, D, split=0) -> int:
     return int(_lib.lib().attn_decode_gqa_workspace_bytes(B, Hq, cap, D, split))
 

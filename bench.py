@@ -222,8 +222,9 @@ def decode_neighbours(iters=50):
     GQA decode workload (B=128) with the new token appended first
     (attn_kv_append with RoPE, then attn_decode_gqa), and the append alone;
     (2) the causal GQA RoPE prefill prompt (S=2048) prefilled in chunks of 32
-    (append the chunk with RoPE, then attn_prefill_chunk) against the one-shot
-    fused prefill.  hipGraph replay, warm."""
+    (attn_prefill_chunk_step per chunk; also as attn_kv_append then
+    attn_prefill_chunk) against the one-shot fused prefill.  hipGraph
+    replay, warm."""
     import torch
     import attention_flash_attn_02_amd as attn
     from workloads import decode_gqa_inputs, prefill_inputs, randn
@@ -261,9 +262,16 @@ def decode_neighbours(iters=50):
     wsc = torch.empty(max(1, attn.prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, S)), dtype=torch.uint8,
                       device=dev)
 
-    # per chunk: append K (rotated) and V, advancing kv_len (one kernel), then
-    # the chunk's attention with its queries rotated in the kernel
+    # per chunk, one call: append K (rotated) and V, the chunk's attention with
+    # its queries rotated in the kernel, and the advance of kv_len in its last
+    # launch (attn_prefill_chunk_step)
     def chunked():
+        Lc.zero_()
+        for (qc, kk, vv), oo in zip(chunks, oc):
+            attn.prefill_chunk_step(qc, kk, vv, kc, vc, Lc, scale, out=oo, workspace=wsc, rope_theta=10000.0)
+
+    # the same as two calls: append with its own advance, then the attention
+    def chunked_two_calls():
         Lc.zero_()
         for (qc, kk, vv), oo in zip(chunks, oc):
             attn.kv_append(kk, vv, kc, vc, Lc, rope_theta=10000.0)
@@ -272,10 +280,12 @@ def decode_neighbours(iters=50):
     fws = torch.empty(attn.prefill_gqa_rope_workspace_bytes(B, Hkv, S, D, torch.bfloat16, 10000.0),
                       dtype=torch.uint8, device=dev)
     mc = time_graph(chunked, 1, 5)
+    m2 = time_graph(chunked_two_calls, 1, 5)
     mf = time_graph(lambda: attn.prefill_gqa_rope(q, k, v, scale, causal=True, rope_theta=10000.0, out=fo,
                                                   workspace=fws), 20, 5)
     flops = prefill_flops(B, Hq, S, D, True)
-    out["chunked_prefill_S2048_T32"] = {"chunked_us": round(mc * 1e3, 2), "one_shot_fused_us": round(mf * 1e3, 2),
+    out["chunked_prefill_S2048_T32"] = {"chunked_us": round(mc * 1e3, 2), "two_calls_per_chunk_us": round(m2 * 1e3, 2),
+                                        "one_shot_fused_us": round(mf * 1e3, 2),
                                         "chunked_tflops": round(flops / (mc * 1e-3) / 1e12, 1),
                                         "chunks": len(chunks)}
     torch.cuda.empty_cache()

@@ -358,6 +358,35 @@ attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v
                                int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
                                float softmax_scale, float rope_theta, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * One step of chunked prefill into a static append cache, in one call
+ * ("Fixed-budget decode audit", "Setup and interpretation": prompts are
+ * prefilled chunk by chunk into the static append cache the decode reads):
+ * the work of attn_kv_append (advance 0) followed by attn_prefill_chunk, with
+ * the cache-length advance carried by the attention's last launch.
+ *   q        [B, Hq, T, D]   the chunk's queries, dtype, not rotated (the
+ *            attention rotates them in registers when rope_theta > 0)
+ *   k_new, v_new [B, Hkv, T, D]  the chunk's keys (not rotated) and values
+ *   k_cache, v_cache [B, Hkv, cap, D]  written at slots L_b .. L_b+T-1 (K
+ *            rotated to those positions when rope_theta > 0; slots >= cap
+ *            are not written)
+ *   kv_len   [B] int32 device memory: on entry L_b, the tokens already
+ *            cached (EXCLUDING the chunk); on return min(L_b + T, cap)
+ *   o, lse, workspace: as attn_prefill_chunk (same workspace size:
+ *            attn_prefill_chunk_workspace_bytes)
+ * Results equal attn_kv_append(..., advance = 1) followed by
+ * attn_prefill_chunk on the same arguments, bit for bit, with one launch
+ * fewer (three kernels: append, attention, combine-and-advance; with a
+ * single key range the advance is a small kernel of its own).  Error
+ * checks are those of both calls and all run before any work is enqueued,
+ * so a rejected call writes nothing; calls sharing kv_len must not overlap.
+ * ------------------------------------------------------------------------ */
+attn_status attn_prefill_chunk_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                    void* v_cache, int32_t* kv_len, void* o, float* lse, void* workspace,
+                                    size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D, int cap,
+                                    int split, attn_dtype dtype, attn_dtype out_dtype, float softmax_scale,
+                                    float rope_theta, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -258,6 +258,24 @@ def test_prefill_chunk_rejects(lib):
     assert chunk(ws=None) == 5 and chunk(wsb=256) == 5 and chunk(ws=P + 16) == 4
 
 
+def test_prefill_chunk_step_rejects(lib):
+    """The fused chunk step fails every host check of the two calls it fuses,
+    before anything is launched (so a rejected call writes nothing)."""
+    def step(q=P, kn=P, vn=P, kc=P, vc=P, L=P, o=P2, lse=None, ws=P, wsb=None, B=2, Hq=16, Hkv=4, T=32, D=128,
+             cap=2056, split=0, dt=_lib.ATTN_BF16, odt=_lib.ATTN_BF16, scale=0.088, theta=0.0):
+        if wsb is None:
+            wsb = lib.attn_prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split)
+        return lib.attn_prefill_chunk_step(q, kn, vn, kc, vc, L, o, lse, ws, wsb, B, Hq, Hkv, T, D, cap, split, dt,
+                                           odt, scale, theta, None)
+    assert step(kn=None) == 1 and step(vn=None) == 1 and step(L=None) == 1 and step(o=None) == 1
+    assert step(T=0) == 2 and step(T=3000) == 2 and step(Hq=6, Hkv=4) == 2 and step(split=100) == 2
+    assert step(scale=0.0) == 2 and step(scale=float("inf")) == 2 and step(theta=float("nan")) == 2
+    assert step(theta=10000.0, cap=70000, T=32) == 6
+    assert step(dt=_lib.ATTN_F32) == 6 and step(D=96) == 6 and step(odt=_lib.ATTN_FP8_E5M2) == 3
+    assert step(kn=ODD) == 4 and step(vn=P + 8) == 4 and step(L=P + 2) == 4 and step(lse=P + 2) == 4
+    assert step(ws=None) == 5 and step(wsb=256) == 5 and step(ws=P + 16) == 4
+
+
 def test_prefill_chunk_workspace_size(lib):
     # partials [B*Hq*T, nsplit, D] f32 then lse [B*Hq*T, nsplit] f32, 256-byte aligned pieces
     B, Hq, Hkv, T, D, cap = 2, 16, 4, 32, 128, 2056

@@ -787,6 +787,99 @@ def test_chunked_prefill_pipeline_equals_fused_prefill(attn, q_rot):
     assert _maxerr(got, to_f64(fused)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("D,G,T,S,split,rope", [(128, 4, 32, 300, 0, True), (64, 2, 17, 200, 0, True),
+                                                (128, 4, 32, 300, 4096, True), (128, 1, 32, 150, 0, False),
+                                                (64, 4, 48, 260, 128, True)])
+def test_prefill_chunk_step_equals_append_then_chunk(attn, D, G, T, S, split, rope):
+    """attn_prefill_chunk_step against the two calls it fuses (kv_append with
+    advance, then prefill_chunk), chunk after chunk over a whole prompt: the
+    outputs, LSEs, both caches and kv_len agree bit for bit after every step,
+    with several key ranges (the combine advances kv_len) and with one (a
+    split covering the cache: the advance is a launch of its own); ragged
+    last chunks; and the chunked result against the oracle's one-shot
+    causal prefill."""
+    B, Hkv = 2, 2
+    Hq, cap = Hkv * G, S + 20
+    q, k, v = prefill_inputs(B, Hq, Hkv, S, D, "bf16", seed=90 + D + T)
+    scale = 1 / math.sqrt(D)
+    theta = 10000.0 if rope else 0.0
+    dq, dk, dv = _dev(q, k, v)
+    caches = [(torch.full((B, Hkv, cap, D), float("nan"), dtype=torch.bfloat16, device="cuda"),
+               torch.full((B, Hkv, cap, D), float("nan"), dtype=torch.bfloat16, device="cuda"),
+               torch.zeros(B, dtype=torch.int32, device="cuda")) for _ in range(2)]
+    ws = torch.empty(max(1, attn.prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap, split)), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for c0 in range(0, S, T):
+        c1 = min(S, c0 + T)
+        qc, kn, vn = (t[:, :, c0:c1].contiguous() for t in (dq, dk, dv))
+        (kc0, vc0, L0), (kc1, vc1, L1) = caches
+        attn.kv_append(kn, vn, kc0, vc0, L0, rope_theta=theta)
+        o0, lse0 = attn.prefill_chunk(qc, kc0, vc0, L0, scale, split=split, workspace=ws, rope_theta=theta,
+                                      return_lse=True)
+        o1, lse1 = attn.prefill_chunk_step(qc, kn, vn, kc1, vc1, L1, scale, split=split, workspace=ws,
+                                           rope_theta=theta, return_lse=True)
+        assert torch.equal(L0, L1) and L1.tolist() == [c1] * B
+        assert torch.equal(o0, o1) and torch.equal(lse0, lse1)
+        assert torch.equal(kc0.view(torch.int16), kc1.view(torch.int16))  # NaN slots compared as bits
+        assert torch.equal(vc0.view(torch.int16), vc1.view(torch.int16))
+        outs.append(o1)
+    want = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), scale, True, theta)
+    assert _maxerr(torch.cat(outs, dim=2), want) <= TOL["bf16"]
+
+
+def test_prefill_chunk_step_graph_replays(attn):
+    """The fused chunk step captured in a hipGraph, one node per chunk, and
+    replayed three times (kv_len reset between replays with a fill kernel):
+    every replay gives the eager outputs, caches and final length."""
+    B, Hq, Hkv, D, T, S = 1, 32, 8, 128, 32, 256
+    cap = S
+    q, k, v = prefill_inputs(B, Hq, Hkv, S, D, "bf16", seed=97)
+    scale = 1 / math.sqrt(D)
+    dq, dk, dv = _dev(q, k, v)
+    chunks = [tuple(t[:, :, c:c + T].contiguous() for t in (dq, dk, dv)) for c in range(0, S, T)]
+    kc = torch.zeros((B, Hkv, cap, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    L = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, attn.prefill_chunk_workspace_bytes(B, Hq, Hkv, T, D, cap)), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.empty_like(c[0]) for c in chunks]
+
+    def run():
+        for (qc, kn, vn), oo in zip(chunks, outs):
+            attn.prefill_chunk_step(qc, kn, vn, kc, vc, L, scale, out=oo, workspace=ws, rope_theta=10000.0)
+    run()
+    torch.cuda.synchronize()
+    want_o = [o.clone() for o in outs]
+    want_k, want_v = kc.clone(), vc.clone()
+    assert L.item() == S
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.zero_()
+        run()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        kc.zero_()
+        vc.zero_()
+        L.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert L.item() == S
+        for o, w in zip(outs, want_o):
+            assert torch.equal(o, w)
+        assert torch.equal(kc, want_k) and torch.equal(vc, want_v)
+        _ = (dq.float() * 2).sum()  # unrelated eager work between replays
+
+
 def test_decode_step_graph_appends_and_attends(attn):
     """A decode step (kv_append with advance, then decode_gqa) captured once in
     a hipGraph and replayed: each replay appends the next token at the slot
