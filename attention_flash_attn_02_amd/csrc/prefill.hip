@@ -34,6 +34,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "prefill_common.hpp"
+#include "rope_common.hpp"
 
 namespace attn {
 
@@ -639,12 +640,36 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
         for (int e = 0; e < 4; ++e) qf[4 * kk + e] = w[e];
       }
     };
+    // chunk mode that appends: this thread's share of the chunk's K (chunk
+    // pairs) and V (chunks) rows, loaded with the query rows, before the key
+    // length is known
+    constexpr int ACPR = D / 16, ACPF = D / 8;  // 16-byte chunk pairs / chunks per 16-bit row
+    constexpr int AKU = (32 * ACPR + 255) / 256, AVU = (32 * ACPF + 255) / 256;
+    const bool app = CHUNK && p.k_new != nullptr;
+    u32x4 ak[CHUNK ? AKU : 1][2], av[CHUNK ? AVU : 1];
     if (CHUNK) {
       load_q();
+      if (app) {
+        const size_t nrow0 = ((size_t)b * p.Hkv + kvh) * p.S;
+        const uint8_t* kn = reinterpret_cast<const uint8_t*>(p.k_new) + nrow0 * ROWB;
+        const uint8_t* vn = reinterpret_cast<const uint8_t*>(p.v_new) + nrow0 * ROWB;
+#pragma unroll
+        for (int u = 0; u < AKU; ++u) {
+          const int w = htid + 256 * u, t = min(w / ACPR, p.S - 1), c = w % ACPR;
+          ak[u][0] = ldg16(kn + (size_t)t * ROWB + 16 * c);
+          ak[u][1] = ldg16(kn + (size_t)t * ROWB + D + 16 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < AVU; ++u) {
+          const int w = htid + 256 * u, t = min(w / ACPF, p.S - 1), c = w % ACPF;
+          av[u] = ldg16(vn + (size_t)t * ROWB + 16 * c);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);  // (the scheduler would otherwise wait for the key length first)
     }
     // key length and query position offset (plain prefill: S and 0)
-    const int Skv = CHUNK ? min(max(p.kv_len[b], 0) + p.kv_add, p.cap) : p.S;
+    const int Lkv = CHUNK ? max(p.kv_len[b], 0) : 0;
+    const int Skv = CHUNK ? min(Lkv + p.kv_add, p.cap) : p.S;
     const int qoff = CHUNK ? Skv - p.S : 0;
     const int kend_all = CAUSAL ? max(0, min(Skv, qoff + p0 + p.P)) : Skv;
     // key range [kbeg, kend) of this item: all keys, or (chunk mode) split
@@ -750,6 +775,33 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
     auto active = [&](int i) {
       return exists(i) && !(CAUSAL && (t0 + HALVES * i + half) * BN > qoff + pw0 + 31);
     };
+
+    // ---- chunk mode that appends: the chunk's rows of this item's key range
+    //      go to the cache (K rotated to slot Lkv + t), and the workgroup
+    //      waits for its stores before any wave loads them back; items of
+    //      the same KV head and range write the same bytes ----
+    if (app) {
+      uint8_t* kcw = const_cast<uint8_t*>(kg);
+      uint8_t* vcw = const_cast<uint8_t*>(vg);
+#pragma unroll
+      for (int u = 0; u < AKU; ++u) {
+        const int w = htid + 256 * u, t = w / ACPR, c = w % ACPR, slot = Lkv + t;
+        if (t < p.S && slot >= kbeg && slot < kend && slot < p.cap) {
+          u32x4 lo = ak[u][0], hi = ak[u][1];
+          if (ROPE == 2) rotate_chunk_pair<Tag>(lo, hi, (float)slot, c, p.rope_fhi, p.rope_fmid, p.rope_flo3);
+          *reinterpret_cast<u32x4*>(kcw + (size_t)slot * ROWB + 16 * c) = lo;
+          *reinterpret_cast<u32x4*>(kcw + (size_t)slot * ROWB + D + 16 * c) = hi;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < AVU; ++u) {
+        const int w = htid + 256 * u, t = w / ACPF, c = w % ACPF, slot = Lkv + t;
+        if (t < p.S && slot >= kbeg && slot < kend && slot < p.cap)
+          *reinterpret_cast<u32x4*>(vcw + (size_t)slot * ROWB + 16 * c) = av[u];
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
 
     // ---- running state ----
     f32x16 acc_o[NDB];
@@ -2066,14 +2118,15 @@ static void launch_chunk_kernel(const PrefillParams& p, bool rope, dim3 grid, di
   else hipLaunchKernelGGL((prefill_fwd_kernel<Tag, D, true, 0, 1, true>), grid, block, 0, st, p);
 }
 
-// the chunk attention: kv_len[b] + kv_add keys per sequence; `adv`, when
-// given, advances kv_len once every reader is done (in the combine, or as a
-// launch of its own when there is a single key range)
+// the chunk attention: kv_len[b] + kv_add keys per sequence; with k_new /
+// v_new the kernel first writes the chunk's rows to the cache itself; `adv`,
+// when given, advances kv_len once every reader is done (in the combine, or
+// as a launch of its own when there is a single key range)
 static attn_status chunk_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
                                    void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq,
                                    int Hkv, int T, int D, int cap, int split, attn_dtype dtype, attn_dtype out_dtype,
                                    float softmax_scale, float rope_theta, int kv_add, KvAdvance adv,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, const void* k_new = nullptr, const void* v_new = nullptr) {
   if (!q || !k_cache || !v_cache || !kv_len || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || cap <= 0 || T > cap) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -2111,6 +2164,8 @@ static attn_status chunk_attention(const void* q, const void* k_cache, const voi
   p.halves = 1;
   p.kv_len = kv_len;
   p.kv_add = kv_add;
+  p.k_new = k_new;
+  p.v_new = v_new;
   p.cap = cap;
   p.nsplit = nsplit;
   p.split_keys = sk;
@@ -2129,6 +2184,10 @@ static attn_status chunk_attention(const void* q, const void* k_cache, const voi
   if (rope) {
     p.rope = 2;
     attn_host::rope_freq_split(rope_theta, D, p.inv_freq, p.rope_fhi, p.rope_flo);
+    if (k_new) {  // the append kernel's three-part split for the keys (the same f_hi)
+      float fhi3[64];
+      attn_host::rope_freq_split(rope_theta, D, nullptr, fhi3, p.rope_flo3, p.rope_fmid);
+    }
   }
   if (dtype == ATTN_BF16) {
     if (D == 64) launch_chunk_kernel<Bf16Tag, 64>(p, rope, grid, block, stream);
@@ -2190,13 +2249,18 @@ extern "C" attn_status attn_prefill_chunk_step(const void* q, const void* k_new,
     const int G = Hq / Hkv, GP = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1, P = 128 / GP;
     if ((long long)((T + P - 1) / P) * B * Hkv * (G / GP) * nsplit > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   }
-  // 1: the chunk's K (rotated to its slots) and V into the caches, kv_len unchanged
-  attn_status st = attn_kv_append(k_new, v_new, nullptr, k_cache, v_cache, kv_len, B, Hkv, 0, T, D, cap, dtype,
-                                  rope_theta, 0, stream);
-  if (st != ATTN_OK) return st;
-  // 2: the attention over kv_len + T keys; 3: the combine, which also
+  // chunks of up to 32 rows: the attention kernel writes the chunk's K
+  // (rotated) and V to the cache itself; longer ones are appended first by
+  // the append kernel (kv_len unchanged)
+  const bool fused = T <= 32;
+  if (!fused) {
+    const attn_status st = attn_kv_append(k_new, v_new, nullptr, k_cache, v_cache, kv_len, B, Hkv, 0, T, D, cap,
+                                          dtype, rope_theta, 0, stream);
+    if (st != ATTN_OK) return st;
+  }
+  // the attention over kv_len + T keys, then the combine, which also
   // advances kv_len by T
   return chunk_attention(q, k_cache, v_cache, kv_len, o, lse, workspace, workspace_bytes, B, Hq, Hkv, T, D, cap,
                          split, dtype, out_dtype, softmax_scale, rope_theta, T, KvAdvance{kv_len, B, T, cap},
-                         stream);
+                         stream, fused ? k_new : nullptr, fused ? v_new : nullptr);
 }

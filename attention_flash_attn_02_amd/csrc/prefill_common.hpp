@@ -37,6 +37,13 @@ struct PrefillParams {
   // chunked prefill against a cache prefix (prefill_fwd_kernel<..., CHUNK>)
   const int* kv_len;  // [B] key lengths (with kv_add: the chunk's tokens), device memory
   int kv_add;         // added to kv_len[b]: 0, or the chunk length when kv_len excludes the chunk
+  // chunk mode that appends the chunk itself (k_new non-null): the chunk's
+  // keys and values [B, Hkv, S, D], written by the kernel to the cache rows
+  // kv_len[b] + t (K rotated there with the three-part frequency split
+  // rope_fhi / rope_fmid / rope_flo3, as the append kernel does)
+  const void* k_new;
+  const void* v_new;
+  float rope_flo3[64];
   int cap;            // cache slots per head
   int nsplit;         // key ranges per item (1: results go straight to o / lse)
   int split_keys;     // keys per range, a multiple of 64

@@ -390,7 +390,8 @@ def prefill_traffic():
 
 
 PREFILL_SOURCES = ("attention_flash_attn_02_amd/csrc/prefill.hip", "attention_flash_attn_02_amd/csrc/prefill_sp.hip",
-                   "attention_flash_attn_02_amd/csrc/prefill_common.hpp", "attention_flash_attn_02_amd/csrc/common.hpp")
+                   "attention_flash_attn_02_amd/csrc/prefill_common.hpp", "attention_flash_attn_02_amd/csrc/common.hpp",
+                   "attention_flash_attn_02_amd/csrc/rope_common.hpp")
 
 
 def cpu_baseline(budget_s=15.0):

@@ -375,9 +375,11 @@ attn_status attn_prefill_chunk(const void* q, const void* k_cache, const void* v
  *   o, lse, workspace: as attn_prefill_chunk (same workspace size:
  *            attn_prefill_chunk_workspace_bytes)
  * Results equal attn_kv_append(..., advance = 1) followed by
- * attn_prefill_chunk on the same arguments, bit for bit, with one launch
- * fewer (three kernels: append, attention, combine-and-advance; with a
- * single key range the advance is a small kernel of its own).  Error
+ * attn_prefill_chunk on the same arguments, bit for bit.  For T <= 32 the
+ * attention kernel writes the chunk's rows to the cache itself, so the step
+ * is two kernels (attention, then the combine, which also advances kv_len;
+ * with a single key range the advance is a small kernel of its own); longer
+ * chunks are appended by the append kernel first.  Error
  * checks are those of both calls and all run before any work is enqueued,
  * so a rejected call writes nothing; calls sharing kv_len must not overlap.
  * ------------------------------------------------------------------------ */
