@@ -73,6 +73,17 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_gqa_kernel(const DecodeGqaP
   uint8_t* ks = stage[wave][1];
   const int m16 = lane & 15, qq = lane >> 4;
   const int wg = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int row0 = b * p.Hq + kvh * p.G;  // first query head (output row) of this KV head
+  // query fragments (B operand of S^T; columns m16 < G are real heads),
+  // loaded before the cache length is read so that the two loads overlap
+  constexpr int NKKQ = D / 32;
+  u32x4 qf[NKKQ];
+  {
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + (size_t)(row0 + min(m16, p.G - 1)) * ROWB;
+#pragma unroll
+    for (int kk = 0; kk < NKKQ; ++kk) qf[kk] = ldg16(qrow + 64 * kk + 16 * qq);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const int L = min(max(p.kv_len[b], 0), p.cap);
   // chunk range of this workgroup, then of this wave
   const int nch = (L + 31) >> 5;
@@ -82,7 +93,6 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_gqa_kernel(const DecodeGqaP
   const int wc0 = min(gc0 + wave * cpw, gc1), wc1 = min(wc0 + cpw, gc1);
   const int s0 = wc0 * 32;
   const int s1 = min(wc1 * 32, L);
-  const int row0 = b * p.Hq + kvh * p.G;  // first query head (output row) of this KV head
 
   f32x4 acc_o[NDB];
 #pragma unroll
@@ -90,14 +100,10 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_gqa_kernel(const DecodeGqaP
   float m_run = kNegInf, l_run = 0.f;
 
   if (s0 < s1) {
-    // query fragments: B operand of S^T (columns m16 < G are real heads)
-    u32x4 qf[NKK];
-    {
-      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + (size_t)(row0 + m16) * ROWB;
+    // columns m16 >= G are not heads: zero them (loaded from head G - 1)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        qf[kk] = m16 < p.G ? ldg16(qrow + 64 * kk + 16 * qq) : u32x4{0, 0, 0, 0};
-    }
+    for (int kk = 0; kk < NKK; ++kk)
+      if (m16 >= p.G) qf[kk] = u32x4{0, 0, 0, 0};
 
     // K and V rows [s0, s1) of this (sequence, KV head) as raw buffers: a slot
     // at or past s1 lies outside the buffer's range, so its load returns zero
