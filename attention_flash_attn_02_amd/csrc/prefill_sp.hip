@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
       k2[NS > 2 ? HALVES * TILEB : 16], k3[NS > 2 ? HALVES * TILEB : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t v0[HALVES * TILEB], v1[HALVES * TILEB],
       v2[NS > 2 ? HALVES * TILEB : 16], v3[NS > 2 ? HALVES * TILEB : 16];
+  __shared__ __attribute__((aligned(16))) float rtab[RQ && HALVES == 1 ? D : 4];  // (after the stages)
   auto kst = [&](auto s) -> uint8_t* {
     constexpr int t = decltype(s)::value % NS;
     if constexpr (t == 0) return k0;
@@ -160,23 +161,17 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
   const int half_items = (n_items + 1) / 2;
   const int item0 = (CAUSAL && !PAIR && wg >= half_items) ? n_items - 1 - (wg - half_items) : wg;
 
-  // RoPE frequencies of this lane's Q elements (element 16 kk + 8 hh + j of
-  // the row pairs with element + D/2; kk < NKK/2, j < 8), read once for every
-  // item: the reads are issued before any load of the first item, so waiting
-  // for them never waits for that item's K/V DMA as well (the vector memory
-  // counter retires in order).  The 8-wave kernel, which has half the
-  // registers, reads them per item.
-  constexpr bool RQ_HOIST = RQ && HALVES == 1;
-  constexpr int NRF = RQ_HOIST ? NKK * 4 : 1;
-  float rfh[NRF], rfl[NRF];
-  if constexpr (RQ_HOIST) {
-#pragma unroll
-    for (int kk = 0; kk < NKK / 2; ++kk)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        rfh[8 * kk + j] = p.rope_fhi[16 * kk + 8 * hh + j];
-        rfl[8 * kk + j] = p.rope_flo[16 * kk + 8 * hh + j];
-      }
+  // RoPE frequencies (the two-part split of each of the D/2 angles): the
+  // 4-wave kernel keeps a copy in LDS that every wave writes itself (the
+  // same values, read back only by the wave that wrote them), so a rotation
+  // reads them with a few LDS loads instead of holding 64 registers through
+  // the key loop; the 8-wave kernel reads them from the parameters per item.
+  constexpr bool RQ_LDS = RQ && HALVES == 1;
+  if constexpr (RQ_LDS) {
+    if (lane < D / 2) {
+      rtab[lane] = p.rope_fhi[lane];
+      rtab[D / 2 + lane] = p.rope_flo[lane];
+    }
   }
 
 #pragma unroll 1
@@ -270,16 +265,33 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
         // element j of k-step kk sits at d = 16 kk + 8 hh + j; its rotate-half
         // partner d + D/2 is in k-step kk + NKK/2 of the same lane
 #pragma unroll
-        for (int kk = 0; kk < NKK / 2; ++kk)
+        for (int kk = 0; kk < NKK / 2; ++kk) {
+          float fhk[8], flk[8];  // frequencies of the 8 elements of k-step kk
+          if constexpr (RQ_LDS) {
+            const f32x4* th = reinterpret_cast<const f32x4*>(rtab + 16 * kk + 8 * hh);
+            const f32x4* tlo = reinterpret_cast<const f32x4*>(rtab + D / 2 + 16 * kk + 8 * hh);
+            const f32x4 h0 = th[0], h1 = th[1], l0 = tlo[0], l1 = tlo[1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              fhk[j] = h0[j];
+              fhk[4 + j] = h1[j];
+              flk[j] = l0[j];
+              flk[4 + j] = l1[j];
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              fhk[j] = p.rope_fhi[16 * kk + 8 * hh + j];
+              flk[j] = p.rope_flo[16 * kk + 8 * hh + j];
+            }
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t w1 = qf[4 * kk + e], w2 = qf[4 * (kk + NKK / 2) + e];
             float r1[2], r2[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-              const int fi = 16 * kk + 8 * hh + 2 * e + s;
-              const float fh = RQ_HOIST ? rfh[(8 * kk + 2 * e + s) % NRF] : p.rope_fhi[fi];
-              const float fl = RQ_HOIST ? rfl[(8 * kk + 2 * e + s) % NRF] : p.rope_flo[fi];
+              const float fh = fhk[2 * e + s], fl = flk[2 * e + s];
               const float rev = __builtin_amdgcn_fractf((float)qpos * fh) + (float)qpos * fl;
               const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
               const float x1 = Tag::to_f32(s ? (w1 >> 16) : (w1 & 0xffff));
@@ -290,6 +302,7 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
             qf[4 * kk + e] = Tag::pack2(r1[0], r1[1]);
             qf[4 * (kk + NKK / 2) + e] = Tag::pack2(r2[0], r2[1]);
           }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < NKK * 4; ++j)
