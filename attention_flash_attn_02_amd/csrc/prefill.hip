@@ -665,6 +665,26 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
           av[u] = ldg16(vn + (size_t)t * ROWB + 16 * c);
         }
       }
+      // tile 0 of this item's key range, before the key length is known:
+      // its address does not depend on it.  The buffer range ends at the
+      // capacity instead of the key length, so the rows from the key length
+      // on hold what the cache held when the load read them; they are fixed
+      // in LDS below, before any use.
+      {
+        const int kb0 = split * p.split_keys;
+        const size_t row0 = ((size_t)b * p.Hkv + kvh) * p.cap + kb0;
+        const int range = max(0, p.cap - kb0) * ROWB;
+        auto early_dma = [&](const void* base, uint8_t* dst, const int* loff) {
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(base) + row0 * ROWB), (short)0, range,
+              kBufferRsrcWord3);
+#pragma unroll
+          for (int u = 0; u < IPW; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_AS(void, dst + RPI * (wq * IPW + u) * ROWB), 16, loff[u], 0, 0, 0);
+        };
+        early_dma(p.k, hbuf, dk);
+        early_dma(p.v, hbuf + 2 * TILEB, dv);
+      }
       __builtin_amdgcn_sched_barrier(0);  // (the scheduler would otherwise wait for the key length first)
     }
     // key length and query position offset (plain prefill: S and 0)
@@ -778,29 +798,72 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
 
     // ---- chunk mode that appends: the chunk's rows of this item's key range
     //      go to the cache (K rotated to slot Lkv + t), and the workgroup
-    //      waits for its stores before any wave loads them back; items of
-    //      the same KV head and range write the same bytes ----
-    if (app) {
-      uint8_t* kcw = const_cast<uint8_t*>(kg);
-      uint8_t* vcw = const_cast<uint8_t*>(vg);
+    //      waits for its stores before any wave loads them back (the loads
+    //      of tiles 1, 2, ...); items of the same KV head and range write
+    //      the same bytes.  Tile 0, loaded before the key length was known,
+    //      then gets the chunk's rows that fall in it and zeros for the V
+    //      rows past the key length (probability 0 times a non-finite value
+    //      would not be 0; the keys there are masked). ----
+    if (CHUNK) {
+      const int key0 = kbeg;
+      const bool fix0 = n_kt > 0 && Skv - key0 < BN;  // tile 0 ends past the key length
+      const bool app0 = app && n_kt > 0 && Lkv < key0 + BN;  // ... or holds chunk rows
+      if (app) {
+        uint8_t* kcw = const_cast<uint8_t*>(kg);
+        uint8_t* vcw = const_cast<uint8_t*>(vg);
 #pragma unroll
-      for (int u = 0; u < AKU; ++u) {
-        const int w = htid + 256 * u, t = w / ACPR, c = w % ACPR, slot = Lkv + t;
-        if (t < p.S && slot >= kbeg && slot < kend && slot < p.cap) {
-          u32x4 lo = ak[u][0], hi = ak[u][1];
-          if (ROPE == 2) rotate_chunk_pair<Tag>(lo, hi, (float)slot, c, p.rope_fhi, p.rope_fmid, p.rope_flo3);
-          *reinterpret_cast<u32x4*>(kcw + (size_t)slot * ROWB + 16 * c) = lo;
-          *reinterpret_cast<u32x4*>(kcw + (size_t)slot * ROWB + D + 16 * c) = hi;
+        for (int u = 0; u < AKU; ++u) {
+          const int w = htid + 256 * u, t = w / ACPR, c = w % ACPR, slot = Lkv + t;
+          if (t < p.S && slot >= kbeg && slot < kend && slot < p.cap) {
+            u32x4 lo = ak[u][0], hi = ak[u][1];
+            if (ROPE == 2) rotate_chunk_pair<Tag>(lo, hi, (float)slot, c, p.rope_fhi, p.rope_fmid, p.rope_flo3);
+            *reinterpret_cast<u32x4*>(kcw + (size_t)slot * ROWB + 16 * c) = lo;
+            *reinterpret_cast<u32x4*>(kcw + (size_t)slot * ROWB + D + 16 * c) = hi;
+            ak[u][0] = lo;
+            ak[u][1] = hi;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < AVU; ++u) {
+          const int w = htid + 256 * u, t = w / ACPF, c = w % ACPF, slot = Lkv + t;
+          if (t < p.S && slot >= kbeg && slot < kend && slot < p.cap)
+            *reinterpret_cast<u32x4*>(vcw + (size_t)slot * ROWB + 16 * c) = av[u];
         }
       }
-#pragma unroll
-      for (int u = 0; u < AVU; ++u) {
-        const int w = htid + 256 * u, t = w / ACPF, c = w % ACPF, slot = Lkv + t;
-        if (t < p.S && slot >= kbeg && slot < kend && slot < p.cap)
-          *reinterpret_cast<u32x4*>(vcw + (size_t)slot * ROWB + 16 * c) = av[u];
+      if (app || fix0) {
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's stores, and its share of tile 0
+        __syncthreads();                // ... and everybody's
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      if (fix0 || app0) {
+        if (fix0) {
+          const int r0 = max(Skv - key0, 0);
+#pragma unroll
+          for (int u = 0; u < BN * CH / 256; ++u) {
+            const int e = htid + 256 * u, r = e / CH, c = e % CH;
+            if (r >= r0) *reinterpret_cast<u32x4*>(vbuf(0) + r * ROWB + 16 * c) = u32x4{0, 0, 0, 0};
+          }
+        }
+        if (app0) {
+#pragma unroll
+          for (int u = 0; u < AKU; ++u) {
+            const int w = htid + 256 * u, t = w / ACPR, c = w % ACPR, slot = Lkv + t;
+            if (t < p.S && slot >= kbeg && slot < kend && slot < p.cap && slot < key0 + BN) {
+              const int r = slot - key0;
+              *reinterpret_cast<u32x4*>(kbuf(0) + r * ROWB + 16 * (c ^ kswz(r))) = ak[u][0];
+              *reinterpret_cast<u32x4*>(kbuf(0) + r * ROWB + 16 * ((c + CH / 2) ^ kswz(r))) = ak[u][1];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < AVU; ++u) {
+            const int w = htid + 256 * u, t = w / ACPF, c = w % ACPF, slot = Lkv + t;
+            if (t < p.S && slot >= kbeg && slot < kend && slot < p.cap && slot < key0 + BN) {
+              const int r = slot - key0;
+              *reinterpret_cast<u32x4*>(vbuf(0) + r * ROWB + 16 * (c ^ vswz(r))) = av[u];
+            }
+          }
+        }
+        __syncthreads();
+      }
     }
 
     // ---- running state ----
@@ -822,7 +885,7 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       if (exists(0)) rotate_store_k(0);
     } else if (RS) {
       if (exists(0)) stage_load(0);
-    } else if (exists(0)) {
+    } else if (exists(0) && !CHUNK) {  // (chunk mode: loaded above)
       dma(kg, kbuf(0), dk, 0);
       dma(vg, vbuf(0), dv, 0);
     }
