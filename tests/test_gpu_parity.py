@@ -732,7 +732,9 @@ def test_kv_append_matches_oracle(attn, dtype, D, T, theta):
                                                     ("f16", 128, 4, 4, 130, 192), ("bf16", 128, 16, 4, 32, 4096)])
 def test_prefill_chunk_matches_oracle(attn, dtype, D, Hq, Hkv, T, split):
     """Chunk rows at positions kv_len - T + t against the cache prefix, with
-    ragged prefixes, NaN in every slot past kv_len (never read) and one
+    ragged prefixes, NaN in every slot past kv_len (the first tile of a key
+    range is loaded before kv_len is known, so these reach LDS: the keys
+    must be masked and the V rows zeroed there) and one
     sequence shorter than the chunk (its leading rows see no key); key ranges
     of the default size, of 64 and 192 keys (merged by the combine kernel,
     with empty ranges) and one range for the whole cache (no workspace)."""
