@@ -157,7 +157,21 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
   const int n_items = p.n_ptiles * per_ptile;
   const int wg = blockIdx.x;
   constexpr bool PAIR = CAUSAL && ATTN_SP_PAIR;
-  const int n_my = PAIR ? (n_items - 1 - wg > wg ? 2 : 1) : 1;
+  // causal pairs, grouped by head: workgroup w = r hp + j takes query tiles
+  // n_ptiles - 1 - j and j of head group r (a long and a short item, the
+  // same amount of work in every workgroup; the pairs in flight share the
+  // K/V of a few heads)
+  // With a head count that is a multiple of 8 the order is also XCD-aware:
+  // workgroups are dealt to the 8 XCDs in turn (w mod 8), so head r goes to
+  // XCD r mod 8 and each XCD takes its heads one after another, keeping a
+  // head's K/V in one L2.
+  const int hp = (p.n_ptiles + 1) / 2;
+  const bool xcd = per_ptile % 8 == 0;
+  const int wx = xcd ? (wg & 7) : 0, wi = xcd ? wg >> 3 : wg;  // XCD, index on it
+  const int per_head = PAIR ? hp : p.n_ptiles;
+  const int pr = xcd ? (wi / per_head) * 8 + wx : wi / per_head;  // head group
+  const int pj = wi % per_head;                                    // pair / query tile of it
+  const int n_my = PAIR ? (p.n_ptiles - 1 - pj > pj ? 2 : 1) : 1;
   const int half_items = (n_items + 1) / 2;
   const int item0 = (CAUSAL && !PAIR && wg >= half_items) ? n_items - 1 - (wg - half_items) : wg;
 
@@ -179,9 +193,13 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
     // every wave is done with the previous item's LDS stages before any
     // wave's loads for this item may land in them
     if (itn > 0) asm volatile("s_barrier" ::: "memory");
-    const int item = itn == 0 ? item0 : n_items - 1 - wg;
-    const int ptile = p.n_ptiles - 1 - item / per_ptile;
-    int rest = item % per_ptile;
+    // unpaired causal items: longest first (query tiles from the last one
+    // down, all heads of a tile together); non-causal ones are all equally
+    // long and go head-major like the pairs (pr, pj above), so the
+    // workgroups in flight share the K/V of a few heads (with all heads in
+    // flight at once, the K/V of a long sequence outgrows the caches)
+    const int ptile = PAIR ? (itn == 0 ? p.n_ptiles - 1 - pj : pj) : CAUSAL ? p.n_ptiles - 1 - item0 / per_ptile : pj;
+    int rest = (PAIR || !CAUSAL) ? pr : item0 % per_ptile;
     const int hg = rest % p.n_hgroups;
     rest /= p.n_hgroups;
     const int kvh = rest % p.Hkv;
@@ -676,8 +694,8 @@ __global__ __launch_bounds__(256 * HALVES, ATTN_SP_WG_PER_CU) void prefill_sp_ke
 
 template <class Tag, int D, bool CAUSAL, bool RQ>
 static void launch_sp_t(const PrefillParams& p, int halves, hipStream_t st) {
-  const long long items = (long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups;
-  const unsigned grid = (unsigned)(CAUSAL && ATTN_SP_PAIR ? (items + 1) / 2 : items);
+  const long long heads = (long long)p.B * p.Hkv * p.n_hgroups;
+  const unsigned grid = (unsigned)(CAUSAL && ATTN_SP_PAIR ? (p.n_ptiles + 1) / 2 * heads : p.n_ptiles * heads);
   if (halves == 2)
     hipLaunchKernelGGL((prefill_sp_kernel<Tag, D, CAUSAL, RQ, ATTN_SP_STAGES, 2>), dim3(grid), dim3(512), 0, st, p);
   else

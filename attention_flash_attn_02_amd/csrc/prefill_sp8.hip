@@ -139,10 +139,24 @@ __global__ __launch_bounds__(256, WPC) void prefill_sp8_kernel(const PrefillPara
     dv[u] = row * ROWB + 16 * (phys ^ vswz(row));
   }
 
-  const int per_ptile = p.B * p.Hkv * p.n_hgroups;
-  const int n_items = p.n_ptiles * per_ptile;
   const int wg = blockIdx.x;
-  const int n_my = CAUSAL ? (n_items - 1 - wg > wg ? 2 : 1) : 1;
+  // causal pairs, grouped by head: workgroup w = r hp + j takes query tiles
+  // n_ptiles - 1 - j and j of head group r (a long and a short item, the
+  // same amount of work in every workgroup; the pairs in flight share the
+  // K/V of a few heads)
+  // With a head count that is a multiple of 8 the order is also XCD-aware:
+  // workgroups are dealt to the 8 XCDs in turn (w mod 8), so head r goes to
+  // XCD r mod 8 and each XCD takes its heads one after another, keeping a
+  // head's K/V in one L2.  Non-causal items are all equally long and go
+  // head-major the same way.
+  const int heads = p.B * p.Hkv * p.n_hgroups;
+  const int hp = (p.n_ptiles + 1) / 2;
+  const bool xcd = heads % 8 == 0;
+  const int wx = xcd ? (wg & 7) : 0, wi = xcd ? wg >> 3 : wg;  // XCD, index on it
+  const int per_head = CAUSAL ? hp : p.n_ptiles;
+  const int pr = xcd ? (wi / per_head) * 8 + wx : wi / per_head;  // head group
+  const int pj = wi % per_head;                                    // pair / query tile of it
+  const int n_my = CAUSAL ? (p.n_ptiles - 1 - pj > pj ? 2 : 1) : 1;
   const float c = p.scale_log2;
   i32x8 ones = {0x3c3c3c3c, 0x3c3c3c3c, 0x3c3c3c3c, 0x3c3c3c3c,
                 0x3c3c3c3c, 0x3c3c3c3c, 0x3c3c3c3c, 0x3c3c3c3c};  // e5m2 1.0
@@ -151,9 +165,8 @@ __global__ __launch_bounds__(256, WPC) void prefill_sp8_kernel(const PrefillPara
 #pragma unroll 1
   for (int itn = 0; itn < n_my; ++itn) {
     if (itn > 0) asm volatile("s_barrier" ::: "memory");
-    const int item = itn == 0 ? wg : n_items - 1 - wg;
-    const int ptile = p.n_ptiles - 1 - item / per_ptile;
-    int rest = item % per_ptile;
+    const int ptile = CAUSAL ? (itn == 0 ? p.n_ptiles - 1 - pj : pj) : pj;
+    int rest = pr;
     const int hg = rest % p.n_hgroups;
     rest /= p.n_hgroups;
     const int kvh = rest % p.Hkv;
@@ -463,8 +476,8 @@ __global__ __launch_bounds__(256, WPC) void prefill_sp8_kernel(const PrefillPara
 #endif
 template <int D, bool CAUSAL>
 static void launch_sp8_t(const PrefillParams& p, hipStream_t st) {
-  const long long items = (long long)p.n_ptiles * p.B * p.Hkv * p.n_hgroups;
-  const unsigned grid = (unsigned)(CAUSAL ? (items + 1) / 2 : items);
+  const long long heads = (long long)p.B * p.Hkv * p.n_hgroups;
+  const unsigned grid = (unsigned)(CAUSAL ? (p.n_ptiles + 1) / 2 * heads : p.n_ptiles * heads);
   constexpr int NS = D == 128 ? ATTN_SP8_NS128 : ATTN_SP8_NS64;
   constexpr int WPC = D == 128 ? ATTN_SP8_WPC128 : ATTN_SP8_WPC64;
   hipLaunchKernelGGL((prefill_sp8_kernel<D, CAUSAL, NS, WPC>), dim3(grid), dim3(256), 0, st, p);
