@@ -568,6 +568,13 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
     dv[u] = row * ROWB + 16 * (phys ^ vswz(row));
   }
 
+  // chunk mode is latency-bound: have every kernel argument the item set-up
+  // reads arrive in one batch of scalar loads (left to themselves, the loads
+  // are issued at first use, one dependent round trip after another)
+  if constexpr (CHUNK)
+    asm volatile("" ::"s"(p.B), "s"(p.Hkv), "s"(p.n_hgroups), "s"(p.n_ptiles), "s"(p.nsplit), "s"(p.G), "s"(p.GP),
+                 "s"(p.P), "s"(p.S), "s"(p.Hq), "s"(p.q), "s"(p.k_new), "s"(p.v_new), "s"(p.k), "s"(p.v),
+                 "s"(p.cap), "s"(p.split_keys), "s"(p.kv_len));
   const int per_ptile = p.B * p.Hkv * p.n_hgroups;
   // (chunk mode: every item is further split into p.nsplit key ranges)
   const int n_items = p.n_ptiles * per_ptile * (CHUNK ? p.nsplit : 1);
@@ -647,7 +654,12 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
     constexpr int AKU = (32 * ACPR + 255) / 256, AVU = (32 * ACPF + 255) / 256;
     const bool app = CHUNK && p.k_new != nullptr;
     u32x4 ak[CHUNK ? AKU : 1][2], av[CHUNK ? AVU : 1];
+    // chunk mode: the key length is read first; its round trip overlaps the
+    // loads below, none of which depends on it
+    int lkv_read = 0;
     if (CHUNK) {
+      lkv_read = p.kv_len[b];
+      __builtin_amdgcn_sched_barrier(0);
       load_q();
       if (app) {
         const size_t nrow0 = ((size_t)b * p.Hkv + kvh) * p.S;
@@ -688,7 +700,9 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
       __builtin_amdgcn_sched_barrier(0);  // (the scheduler would otherwise wait for the key length first)
     }
     // key length and query position offset (plain prefill: S and 0)
-    const int Lkv = CHUNK ? max(p.kv_len[b], 0) : 0;
+    // (moved to a scalar register only here: converted at the load, the
+    // value would be waited for before the loads above were issued)
+    const int Lkv = CHUNK ? max(__builtin_amdgcn_readfirstlane(lkv_read), 0) : 0;
     const int Skv = CHUNK ? min(Lkv + p.kv_add, p.cap) : p.S;
     const int qoff = CHUNK ? Skv - p.S : 0;
     const int kend_all = CAUSAL ? max(0, min(Skv, qoff + p0 + p.P)) : Skv;
