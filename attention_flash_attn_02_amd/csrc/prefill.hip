@@ -443,6 +443,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   }
 }
 
+// cache policy of the chunk-mode row stores (16: sc1, device scope)
+#ifndef ATTN_CHUNK_OAUX
+#define ATTN_CHUNK_OAUX 16
+#endif
+
 // ---------------------------------------------------------------------------
 // MFMA kernel, 16-bit inputs: 8 waves per workgroup.
 //
@@ -1252,10 +1257,16 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
             const int r = RPR * i + ln / CPR, c = ln % CPR;
             ov[i] = *reinterpret_cast<const u32x4*>(area + r * RB + 16 * (c ^ (r % CPR)));
           }
+          // stores at device scope (sc1) through a buffer whose range ends
+          // after this wave's last row in the chunk (rows past it, or a wave
+          // with none, are dropped): measured 952 -> 933 us on the chunked
+          // 2048-token prompt against plain stores, 961 with non-temporal sc1
+          const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+              obase, (short)0, (int)(max(0, min(p.S - pw0, 32)) * rstride), kBufferRsrcWord3);
 #pragma unroll
           for (int i = 0; i < 32 / RPR; ++i) {
             const int r = RPR * i + ln / CPR, c = ln % CPR;
-            if (pw0 + r < p.S) *reinterpret_cast<u32x4*>(obase + (size_t)r * rstride + 16 * c) = ov[i];
+            __builtin_amdgcn_raw_buffer_store_b128(ov[i], ors, (int)(r * rstride) + 16 * c, 0, ATTN_CHUNK_OAUX);
           }
         };
         if (to_ws || p.out_dtype == ATTN_F32) stage_out(ic_t<ATTN_F32>{});
