@@ -62,6 +62,15 @@ __device__ inline float max3(float a, float b, float c) {
   return r;
 }
 
+// 16-bit O through LDS, for whole-row stores (1: on), and the cache policy
+// of those stores (16: sc1, device scope)
+#ifndef ATTN_SP8_OLDS
+#define ATTN_SP8_OLDS 1
+#endif
+#ifndef ATTN_SP8_OAUX
+#define ATTN_SP8_OAUX 16
+#endif
+
 // NS: LDS stages per tensor; WPC: workgroups per compute unit the register
 // allocation is made for (2: two waves per SIMD, at most 256 registers each)
 template <int D, bool CAUSAL, int NS, int WPC>
@@ -444,6 +453,69 @@ __global__ __launch_bounds__(256, WPC) void prefill_sp8_kernel(const PrefillPara
     // masked tiles, never happens: its maximum is -inf) ----
     const float l = acc_l[0];
     const float inv = l > 0.f ? p.out_scale / l : 0.f;
+#if ATTN_SP8_OLDS
+    if (p.out_dtype != ATTN_F32) {
+      // 16-bit O leaves through LDS, so that every store instruction writes
+      // 16-byte pieces of whole rows (a lane's accumulator holds 4-element
+      // pieces of one row: stored directly, each instruction touches 32
+      // rows).  Wave w transposes through stage array w (a 64-key fp8 tile
+      // holds exactly 32 rows of 16-bit output) once every wave is past its
+      // key loop and the loads into the stages have landed; the barrier at
+      // the start of the next item keeps that item's loads out until all
+      // waves have read their rows back.
+      uint8_t* area = wave == 0 ? k0 : wave == 1 ? k1 : wave == 2 ? v0 : v1;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("s_barrier" ::: "memory");
+      if (n_w > 0) {
+        int lm = m, ln = lane;
+        asm volatile("" : "+v"(lm), "+v"(ln));  // keep the addresses below out of the item loop
+        auto stage_out = [&](auto odt) {
+          constexpr int OD = decltype(odt)::value;
+          constexpr int RB = D * 2;        // bytes per output row
+          constexpr int CPR = RB / 16;     // 16-byte pieces per row (XOR-swizzled by row)
+          constexpr int RPR = 64 / CPR;    // rows per read instruction
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int byte = (32 * db + 8 * g4 + 4 * hh) * 2;
+              uint8_t* dst = area + lm * RB + 16 * ((byte / 16) ^ (lm % CPR)) + byte % 16;
+              const float o0 = acc_o[db][4 * g4] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
+              const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;
+              if constexpr (OD == ATTN_BF16) *reinterpret_cast<u32x2*>(dst) = u32x2{Bf16Tag::pack2(o0, o1), Bf16Tag::pack2(o2, o3)};
+              else *reinterpret_cast<u32x2*>(dst) = u32x2{F16Tag::pack2(o0, o1), F16Tag::pack2(o2, o3)};
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes are done before its reads
+          // all reads first, then all stores; the buffer range ends at the
+          // sequence end, so rows past it are dropped without a branch
+          // (the base is moved to scalar registers explicitly: built from
+          // values the compiler had placed in vector registers, the buffer
+          // descriptor would be wrapped in a loop over its distinct values)
+          const uint64_t oa = reinterpret_cast<uint64_t>(reinterpret_cast<uint8_t*>(p.o) +
+                                                         (((size_t)b * p.Hq + head) * p.S + pw0) * RB);
+          uint8_t* obase = reinterpret_cast<uint8_t*>(
+              ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(oa >> 32)) << 32) |
+              (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)oa));
+          const int orange = __builtin_amdgcn_readfirstlane(max(0, min(p.S - pw0, 32)) * RB);
+          const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, orange, kBufferRsrcWord3);
+          u32x4 ov[32 / RPR];
+#pragma unroll
+          for (int i = 0; i < 32 / RPR; ++i) {
+            const int r = RPR * i + ln / CPR, c = ln % CPR;
+            ov[i] = *reinterpret_cast<const u32x4*>(area + r * RB + 16 * (c ^ (r % CPR)));
+          }
+#pragma unroll
+          for (int i = 0; i < 32 / RPR; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(ov[i], ors, (RPR * i + ln / CPR) * RB + 16 * (ln % CPR), 0,
+                                                   ATTN_SP8_OAUX);
+        };
+        if (p.out_dtype == ATTN_BF16) stage_out(ic8<ATTN_BF16>{});
+        else stage_out(ic8<ATTN_F16>{});
+        if (p.lse && hh == 0 && qpos < p.S)
+          p.lse[((size_t)b * p.Hq + head) * p.S + qpos] = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : kNegInf;
+      }
+    } else
+#endif
     if (qpos < p.S && n_w > 0) {
       const size_t row = ((size_t)b * p.Hq + head) * p.S + qpos;
 #pragma unroll
