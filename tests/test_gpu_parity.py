@@ -409,6 +409,24 @@ def test_fp8_e4m3_p_full(attn, D, causal, config):
         assert _maxerr(o, want) <= TOL["fp8_e5m2"]
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("B,H,N,D,causal", [(1, 8, 333, 64, False), (1, 3, 200, 128, True), (2, 4, 77, 128, True)])
+def test_fp8_16bit_output_every_element(attn, out_dtype, B, H, N, D, causal):
+    """fp8 inputs written as 16-bit output: the pipelined fp8 kernel moves O
+    through LDS and stores whole rows through a buffer whose range ends at the
+    sequence end.  Ragged lengths leave the last query tile part-filled (and
+    at N=77 whole waves without a row); 8 heads (one sequence of 8, or two of
+    4) take the XCD-dealt work order, 3 the plain one.  Every element and the
+    LSE against the oracle."""
+    q, k, v = prefill_inputs(B, H, H, N, D, "fp8_e5m2", seed=N + D + H)
+    o, lse = attn.prefill_gqa_rope(*_dev(q, k, v), 1 / math.sqrt(D), causal=causal, out_dtype=out_dtype,
+                                   return_lse=True)
+    assert o.dtype == out_dtype
+    want, want_lse = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal, return_lse=True)
+    assert _maxerr(o, want) <= TOL["fp8_e5m2"]
+    assert _maxerr(lse, want_lse) <= TOL["fp8_e5m2"]
+
+
 def test_prefill_descales(attn):
     q, k, v = prefill_inputs(1, 4, 4, 100, 64, "fp8_e5m2", seed=9)
     o = attn.prefill_gqa_rope(*_dev(q, k, v), 0.125, causal=True, q_descale=0.5, k_descale=2.0,
