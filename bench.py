@@ -449,6 +449,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only GQA and MLA decode at batch 128 with the default splits, `steps` calls "
                          "each (for profiling runs); prints one JSON line of its own")
+    ap.add_argument("--neighbours-only", action="store_true",
+                    help="only the append + decode step and the chunked prefill prompt (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true", help="skip the tile-config sweep")
     ap.add_argument("--prefill-config", type=int, default=None,
@@ -508,6 +510,11 @@ def main():
             out[f"decode_{kind}_B128"] = r
             log(f"decode {kind} B=128:", json.dumps(r))
         print(json.dumps({"decode_only": out}), flush=True)
+        return
+    if args.neighbours_only:
+        out = decode_neighbours()
+        log("decode neighbours:", json.dumps(out))
+        print(json.dumps({"neighbours_only": out}), flush=True)
         return
 
     # ---- the step: causal GQA prefill with fused RoPE, full workload ----
