@@ -122,12 +122,15 @@ __global__ __launch_bounds__(256) void combine_kernel_v4s(const float* __restric
 }
 
 // Parts stored as bf16 bits (half the bytes of fp32 parts; used by the MLA
-// decode, whose parts are 448 wide): one thread per (row, 4 dims), the loop
-// of combine_kernel_v4 over 8-byte loads.
+// decode, whose parts are 448 wide, and by chunked prefill): one thread per
+// (row, 4 dims), the loop of combine_kernel_v4 over 8-byte loads; optional
+// merged LSE and kv_len advance as in combine_kernel_v4.
 __global__ __launch_bounds__(256) void combine_kernel_v4_bf16(const uint16_t* __restrict__ o_part,
                                                               const float* __restrict__ lse_part,
-                                                              void* __restrict__ o, int R, int nsplit, int D,
-                                                              int out_dtype) {
+                                                              void* __restrict__ o, float* __restrict__ lse_out,
+                                                              int R, int nsplit, int D, int out_dtype,
+                                                              KvAdvance adv) {
+  kv_advance(adv);
   const int d4n = D >> 2;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   if (t >= (long long)R * d4n) return;
@@ -138,6 +141,7 @@ __global__ __launch_bounds__(256) void combine_kernel_v4_bf16(const uint16_t* __
   const size_t oidx = (size_t)r * D + d;
   if (mx == kNegInf) {
     store4(o, oidx, out_dtype, 0.f, 0.f, 0.f, 0.f);
+    if (lse_out && d == 0) lse_out[r] = kNegInf;
     return;
   }
   const u32x2* op = reinterpret_cast<const u32x2*>(o_part + (size_t)r * nsplit * D + d);
@@ -165,13 +169,14 @@ __global__ __launch_bounds__(256) void combine_kernel_v4_bf16(const uint16_t* __
   }
   const float inv = 1.f / wsum;
   store4(o, oidx, out_dtype, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  if (lse_out && d == 0) lse_out[r] = mx + __log2f(wsum) * kLn2;
 }
 
 void launch_combine_bf16_parts(const uint16_t* o_part, const float* lse_part, void* o, int R, int nsplit,
-                               int D, int out_dtype, hipStream_t stream) {
+                               int D, int out_dtype, hipStream_t stream, float* lse_out, KvAdvance adv) {
   const long long threads = (long long)R * (D / 4);
   hipLaunchKernelGGL(combine_kernel_v4_bf16, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, o_part,
-                     lse_part, o, R, nsplit, D, out_dtype);
+                     lse_part, o, lse_out, R, nsplit, D, out_dtype, adv);
 }
 
 // General D: one wave per row, four rows per workgroup.  Lane s holds split

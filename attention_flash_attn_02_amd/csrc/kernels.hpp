@@ -23,7 +23,8 @@ void launch_combine(const float* o_part, const float* lse_part, void* o, int R, 
 
 // The same with the partial outputs stored as bf16 bits (o_part [R, nsplit, D]).
 void launch_combine_bf16_parts(const uint16_t* o_part, const float* lse_part, void* o, int R, int nsplit,
-                               int D, int out_dtype, hipStream_t stream);
+                               int D, int out_dtype, hipStream_t stream, float* lse_out = nullptr,
+                               KvAdvance adv = {});
 
 // kv_len[b] = min(kv_len[b] + T, cap) as a launch of its own
 void launch_kv_advance(const KvAdvance& adv, hipStream_t stream);

@@ -443,6 +443,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   }
 }
 
+// chunk mode with several key ranges: the ranges' parts in bf16 (1) or fp32 (0)
+#ifndef ATTN_CHUNK_BF16_PARTS
+#define ATTN_CHUNK_BF16_PARTS 1
+#endif
 // cache policy of the chunk-mode row stores (16: sc1, device scope)
 #ifndef ATTN_CHUNK_OAUX
 #define ATTN_CHUNK_OAUX 16
@@ -1269,7 +1273,8 @@ __global__ __launch_bounds__(256 * HALVES, BNT == 32 ? 3 : 2) void prefill_fwd_k
             __builtin_amdgcn_raw_buffer_store_b128(ov[i], ors, (int)(r * rstride) + 16 * c, 0, ATTN_CHUNK_OAUX);
           }
         };
-        if (to_ws || p.out_dtype == ATTN_F32) stage_out(ic_t<ATTN_F32>{});
+        if (to_ws) stage_out(ic_t<ATTN_CHUNK_BF16_PARTS ? ATTN_BF16 : ATTN_F32>{});
+        else if (p.out_dtype == ATTN_F32) stage_out(ic_t<ATTN_F32>{});
         else if (p.out_dtype == ATTN_BF16) stage_out(ic_t<ATTN_BF16>{});
         else stage_out(ic_t<ATTN_F16>{});
         if (qpos < p.S && hh == 0) {
@@ -2284,7 +2289,10 @@ static attn_status chunk_attention(const void* q, const void* k_cache, const voi
     if (D == 64) launch_chunk_kernel<F16Tag, 64>(p, rope, grid, block, stream);
     else launch_chunk_kernel<F16Tag, 128>(p, rope, grid, block, stream);
   }
-  if (nsplit > 1) launch_combine(p.ws_o, p.ws_lse, o, (int)R, nsplit, D, out_dtype, stream, lse, adv);
+  if (nsplit > 1 && ATTN_CHUNK_BF16_PARTS)
+    launch_combine_bf16_parts(reinterpret_cast<const uint16_t*>(p.ws_o), p.ws_lse, o, (int)R, nsplit, D, out_dtype,
+                              stream, lse, adv);
+  else if (nsplit > 1) launch_combine(p.ws_o, p.ws_lse, o, (int)R, nsplit, D, out_dtype, stream, lse, adv);
   else if (adv.kv_len) launch_kv_advance(adv, stream);
   return attn_host::launch_status();
 }

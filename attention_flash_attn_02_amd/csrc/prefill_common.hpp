@@ -47,7 +47,7 @@ struct PrefillParams {
   int cap;            // cache slots per head
   int nsplit;         // key ranges per item (1: results go straight to o / lse)
   int split_keys;     // keys per range, a multiple of 64
-  float* ws_o;        // [B*Hq*S, nsplit, D] partial outputs (nsplit > 1)
+  float* ws_o;        // [B*Hq*S, nsplit, D] partial outputs (nsplit > 1; bf16 bits in chunk mode)
   float* ws_lse;      // [B*Hq*S, nsplit] partial log-sum-exps (nsplit > 1)
 };
 
